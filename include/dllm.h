@@ -1,0 +1,178 @@
+/*
+ * dllm.h -- C ABI of the token-skipping denoising-step library for AMD Instinct MI355X (gfx950).
+ *
+ * One denoising step of a masked-diffusion LLM (LLaDA / Dream shaped) that recomputes only
+ * salient tokens and reuses cached state for the rest, split into five calls:
+ *
+ *   dllm_saliency               per-token importance score
+ *   dllm_select_compact         top-k or threshold selection + stream compaction
+ *   dllm_gather_qkv_scatter_kv  QKV projection of the selected tokens, K/V scattered into the cache
+ *   dllm_partial_attn           selected queries against the whole (updated) K/V cache, no mask
+ *   dllm_gather_ffn_scatter     output projection + SwiGLU FFN of the selected tokens, scattered
+ *                               back into the cached hidden states
+ *
+ * Sources (web pages; section names as printed there):
+ *   [ES-dLLM]  "ES-dLLM: Efficient Inference for Diffusion Large Language Models by Early-Skipping",
+ *              German summary page §2.A (importance-score equation, alpha = 0.5) and §2.B (top-k
+ *              positions proceed; K/V/hidden caches updated in place for selected tokens, old
+ *              entries reused for skipped ones; skip at early layers such as 1/8 and 1/4 depth);
+ *              Dutch summary page, "Methodologie".
+ *   [DyLLM]    "DyLLM: Efficient Diffusion LLM Inference via Saliency-based Token Selection and
+ *              Partial Attention", French summary page §1 (bidirectional attention, each step a
+ *              prefill-like pass), §2.A (cosine similarity of step t and t-1 vectors, salient below a
+ *              threshold tau; FFN skipped for stable tokens), §2.B (attention rows of salient tokens
+ *              recomputed exactly).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned, row-major and
+ *     contiguous with the layouts given below. The library allocates nothing and keeps no mutable
+ *     global state; calls are re-entrant.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously; no
+ *     call synchronises the device.
+ *   - All arguments are validated on the host before anything is enqueued. A return value other
+ *     than DLLM_OK means nothing was enqueued and nothing was written. Execution faults surface at
+ *     the caller's next synchronisation.
+ *   - One storage type per call (shape->dtype) covers every tensor except: scores, confidences and
+ *     deltas are float32; indices are int32; the force mask is uint8.
+ *   - bf16 tensors are multiplied on the matrix cores with float32 accumulation; norms, softmax
+ *     and SwiGLU are evaluated in float32.
+ */
+#ifndef DLLM_H_
+#define DLLM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DLLM_OK = 0,
+  DLLM_ERR_INVALID_ARG = 1,   /* NULL required pointer, bad dimension, bad enum, misaligned ptr */
+  DLLM_ERR_UNSUPPORTED = 2,   /* valid but outside this build: hd not 64/128, d or F % 64 != 0 ... */
+  DLLM_ERR_WORKSPACE = 3,     /* ws_bytes smaller than dllm_workspace_bytes() */
+  DLLM_ERR_HIP = 4            /* a kernel launch was rejected by the runtime */
+} dllm_status;
+
+typedef enum { DLLM_F32 = 0, DLLM_BF16 = 1 } dllm_dtype;
+
+/* Per-token variation between step t and t-1 (x = current, y = previous vector, length d). */
+typedef enum {
+  DLLM_DELTA_L1N = 0,  /* ||x - y||_1 / (sqrt(d) ||y||_2)     [ES-dLLM] §2.A equation (default) */
+  DLLM_DELTA_COS = 1,  /* 1 - <x,y> / (||x|| ||y||)            [DyLLM] §2.A cosine rule          */
+  DLLM_DELTA_L2R = 2   /* ||x - y||_2 / ||y||_2                 relative L2 change                */
+} dllm_delta;
+
+typedef enum { DLLM_SEL_THRESHOLD = 0, DLLM_SEL_TOPK = 1 } dllm_sel_mode;
+
+typedef enum {
+  DLLM_OP_SALIENCY = 0, DLLM_OP_SELECT = 1, DLLM_OP_QKV = 2, DLLM_OP_ATTN = 3, DLLM_OP_FFN = 4
+} dllm_op;
+
+/* Model / batch shape. 48 bytes, no implicit padding.
+ *   B batch rows (sequences), S positions per sequence, d model width, H query heads,
+ *   Hkv key/value heads (H % Hkv == 0; query head h reads kv head h / (H / Hkv)), hd head width,
+ *   F FFN inner width, dtype a dllm_dtype, V vocabulary size (saliency only), rms_eps RMSNorm
+ *   epsilon. */
+typedef struct {
+  int32_t B, S, d, H, Hkv, hd, F;
+  int32_t dtype;
+  int64_t V;
+  float rms_eps;
+  int32_t reserved; /* must be 0 */
+} dllm_shape;
+
+#define DLLM_MAX_SELECT_S 8192 /* largest S dllm_select_compact accepts (one row lives in LDS) */
+
+/* (1) Saliency [ES-dLLM §2.A equation; DyLLM §2.A].
+ *   score[b,s] = alpha * c[b,s] + (1 - alpha) * delta[b,s]
+ *   c     = max_v softmax(logits[b,s,:])  (largest probability at temperature 1, previous step)
+ *   delta = variation of h_cur[b,s,:] against h_prev[b,s,:] of kind `delta_kind`.
+ * h_cur, h_prev : [B,S,d] dtype; may be NULL only when alpha == 1. d % 8 == 0.
+ * logits        : [B,S,V] dtype; may be NULL only when alpha == 0.
+ * score         : [B,S] float32 (required).
+ * conf_out      : [B,S] float32 or NULL (requires logits).
+ * delta_out     : [B,S] float32 or NULL (requires h_cur/h_prev).
+ * alpha in [0,1]. With alpha == 0 and conf_out == NULL the logits are not read.
+ * Workspace: none. */
+dllm_status dllm_saliency(const dllm_shape* shape, int32_t delta_kind, float alpha,
+                          const void* h_cur, const void* h_prev, const void* logits,
+                          float* score, float* conf_out, float* delta_out, void* stream);
+
+/* (2) Selection + stream compaction [ES-dLLM §2.B top-k; DyLLM §2.A threshold].
+ * Per sequence b, the selected set is force[b,:] plus
+ *   TOPK:      the k best non-forced positions by (score descending, position ascending), where
+ *              NaN ranks below -inf and -0 equals +0 (fewer than k candidates -> all of them);
+ *   THRESHOLD: the non-forced positions with score > tau (float32 compare; NaN never passes).
+ * Output: sel_idx[row_ptr[b] .. row_ptr[b+1]) holds the flat ids b*S + s of sequence b in
+ * ascending order; row_ptr[0] = 0, row_ptr[B] = total count M. Bit-exact and deterministic.
+ * score : [B,S] float32; force : [B,S] uint8 (nonzero = forced) or NULL.
+ * sel_idx : int32 [B*S] (entries past row_ptr[B] untouched); row_ptr : int32 [B+1].
+ * S <= DLLM_MAX_SELECT_S, else DLLM_ERR_UNSUPPORTED. k >= 0; tau not NaN.
+ * Workspace: none (ws may be NULL). */
+dllm_status dllm_select_compact(const dllm_shape* shape, int32_t mode, float tau, int32_t k,
+                                const float* score, const uint8_t* force,
+                                int32_t* sel_idx, int32_t* row_ptr,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* (3) Gathered QKV projection + K/V cache scatter [ES-dLLM §2.B partial cache update].
+ * For j < M = min(row_ptr[B], m_cap), with (b, s) = (sel_idx[j] / S, sel_idx[j] % S):
+ *   xn = h_in[b,s,:] / sqrt(mean(h_in[b,s,:]^2) + rms_eps) * g_attn
+ *   [q | k | v] = xn W_qkv^T
+ *   q_sel[j,:] = q;  k_cache[b,hk,s,:] = k[hk];  v_cache[b,hk,s,:] = v[hk]
+ * h_in    : [B,S,d];  g_attn : [d];  w_qkv : [(H + 2 Hkv) hd, d] rows ordered Q | K | V
+ * q_sel   : [m_cap, H hd];  k_cache, v_cache : [B, Hkv, S, hd], entries of unselected positions
+ *           are never written.
+ * m_cap   : capacity in rows (0 <= m_cap <= B S). M is read on the device, so no host sync.
+ * hd in {64,128}; d % 64 == 0. Workspace: dllm_workspace_bytes(DLLM_OP_QKV, shape, m_cap). */
+dllm_status dllm_gather_qkv_scatter_kv(const dllm_shape* shape,
+                                       const void* h_in, const void* g_attn, const void* w_qkv,
+                                       const int32_t* sel_idx, const int32_t* row_ptr,
+                                       int32_t m_cap, void* q_sel, void* k_cache, void* v_cache,
+                                       void* ws, size_t ws_bytes, void* stream);
+
+/* (4) Partial attention [DyLLM §2.B exact rows for salient queries; §1 bidirectional].
+ * For j < M and query head h (kv head hk = h / (H / Hkv)), with b = sel_idx[j] / S:
+ *   o_sel[j, h hd : (h+1) hd] = sum_t softmax_t(scale * q . k_cache[b,hk,t,:]) v_cache[b,hk,t,:]
+ * over every t in [0, S): no mask, the token itself and masked positions included.
+ * q_sel : [m_cap, H hd];  k_cache, v_cache : [B, Hkv, S, hd];  o_sel : [m_cap, H hd].
+ * scale finite (usually 1/sqrt(hd)). hd in {64,128}.
+ * Workspace: dllm_workspace_bytes(DLLM_OP_ATTN, shape, m_cap) (split-key partials). */
+dllm_status dllm_partial_attn(const dllm_shape* shape, float scale,
+                              const void* q_sel, const void* k_cache, const void* v_cache,
+                              const int32_t* sel_idx, const int32_t* row_ptr, int32_t m_cap,
+                              void* o_sel, void* ws, size_t ws_bytes, void* stream);
+
+/* (5) Gathered output projection + SwiGLU FFN + hidden-state scatter [DyLLM §2.A FFN only for
+ * salient tokens; ES-dLLM §2.B hidden-state cache updated in place].
+ * For j < M with (b, s) = (sel_idx[j] / S, sel_idx[j] % S):
+ *   h  = h_in[b,s,:] + o_sel[j,:] W_o^T
+ *   hn = h / sqrt(mean(h^2) + rms_eps) * g_ffn
+ *   h_out[b,s,:] = h + (silu(hn W_gate^T) * (hn W_up^T)) W_down^T,  silu(x) = x / (1 + e^-x)
+ * h_in : [B,S,d]; o_sel : [m_cap, H hd]; w_o : [d, H hd]; g_ffn : [d]; w_gate, w_up : [F, d];
+ * w_down : [d, F]; h_out : [B,S,d], rows of unselected positions are never written. h_out may
+ * alias h_in. d % 64 == 0, F % 64 == 0, hd in {64,128}.
+ * Workspace: dllm_workspace_bytes(DLLM_OP_FFN, shape, m_cap). */
+dllm_status dllm_gather_ffn_scatter(const dllm_shape* shape,
+                                    const void* h_in, const void* o_sel, const void* w_o,
+                                    const void* g_ffn, const void* w_gate, const void* w_up,
+                                    const void* w_down, const int32_t* sel_idx,
+                                    const int32_t* row_ptr, int32_t m_cap, void* h_out,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace the call `op` (a dllm_op) needs for this shape and m_cap; 0 when
+ * none. Returns (size_t)-1 for an invalid op or shape. Pure host function. */
+size_t dllm_workspace_bytes(int32_t op, const dllm_shape* shape, int32_t m_cap);
+
+/* Static, NUL-terminated name of a dllm_status value. */
+const char* dllm_status_string(int32_t status);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t dllm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLLM_H_ */

@@ -261,23 +261,24 @@ def dense_layer(h, wts: dict, H: int, Hkv: int, hd: int, eps: float, scale: floa
     f = {k: np.asarray(v, dtype=np.float64) for k, v in wts.items()}
     ms = np.mean(h ** 2, axis=2, keepdims=True)
     xn = h * (1.0 / np.sqrt(ms + eps)) * f["g_attn"]
-    qkv = np.einsum("bsd,nd->bsn", xn, f["w_qkv"])
+    qkv = (xn.reshape(B * S, d) @ f["w_qkv"].T).reshape(B, S, -1)
     q = qkv[..., : H * hd].reshape(B, S, H, hd).transpose(0, 2, 1, 3)          # [B,H,S,hd]
     k = qkv[..., H * hd: (H + Hkv) * hd].reshape(B, S, Hkv, hd).transpose(0, 2, 1, 3)
     v = qkv[..., (H + Hkv) * hd:].reshape(B, S, Hkv, hd).transpose(0, 2, 1, 3)
-    k_rep = np.repeat(k, G, axis=1)                                              # [B,H,S,hd]
-    v_rep = np.repeat(v, G, axis=1)
-    logit = np.einsum("bhqe,bhte->bhqt", q, k_rep) * scale
-    w = np.exp(logit - logit.max(axis=3, keepdims=True))
-    w = w / w.sum(axis=3, keepdims=True)
-    o = np.einsum("bhqt,bhte->bhqe", w, v_rep).transpose(0, 2, 1, 3).reshape(B, S, H * hd)
-    h1 = h + np.einsum("bse,de->bsd", o, f["w_o"])
+    o = np.zeros((B, S, H, hd))
+    for b in range(B):
+        for hh in range(H):
+            logit = (q[b, hh] @ k[b, hh // G].T) * scale                           # [S, S]
+            w = np.exp(logit - logit.max(axis=1, keepdims=True))
+            w = w / w.sum(axis=1, keepdims=True)
+            o[b, :, hh, :] = w @ v[b, hh // G]
+    h1 = h + (o.reshape(B * S, H * hd) @ f["w_o"].T).reshape(B, S, d)
     ms1 = np.mean(h1 ** 2, axis=2, keepdims=True)
-    hn = h1 * (1.0 / np.sqrt(ms1 + eps)) * f["g_ffn"]
-    gate = np.einsum("bsd,fd->bsf", hn, f["w_gate"])
-    up = np.einsum("bsd,fd->bsf", hn, f["w_up"])
+    hn = (h1 * (1.0 / np.sqrt(ms1 + eps)) * f["g_ffn"]).reshape(B * S, d)
+    gate = hn @ f["w_gate"].T
+    up = hn @ f["w_up"].T
     act = gate / (1.0 + np.exp(-gate)) * up
-    y = h1 + np.einsum("bsf,df->bsd", act, f["w_down"])
+    y = h1 + (act @ f["w_down"].T).reshape(B, S, d)
     return k, v, y
 
 

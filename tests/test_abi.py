@@ -1,0 +1,145 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/dllm.h declares, sizes
+workspaces on the host, and rejects bad arguments before enqueuing anything.
+
+The pointers passed below are fake (aligned integers): every case is rejected by host-side
+validation, so nothing is ever dereferenced or launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_skipping_partial_amd as tsp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dllm.h")
+
+P = 0x10000  # fake, 16-byte aligned "device" pointer
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dllm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("dllm_saliency", "dllm_select_compact", "dllm_gather_qkv_scatter_kv",
+              "dllm_partial_attn", "dllm_gather_ffn_scatter"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tsp.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(tsp.EXPORTS) == set(declared_functions())
+
+
+def test_shape_struct_layout():
+    assert ctypes.sizeof(tsp.Shape) == 48
+    assert tsp.Shape.V.offset == 32 and tsp.Shape.rms_eps.offset == 40
+
+
+def test_status_strings_and_version():
+    assert tsp.status_string(0) == "DLLM_OK"
+    assert tsp.status_string(3) == "DLLM_ERR_WORKSPACE"
+    assert tsp.status_string(99) == "DLLM_ERR_UNKNOWN"
+    assert tsp.version() >= 100
+
+
+def llada(B=1, S=1024, dtype="bf16"):
+    return tsp.Shape(B=B, S=S, d=4096, H=32, Hkv=32, hd=128, F=12288, dtype=dtype, V=126464)
+
+
+def test_workspace_sizes():
+    s = llada()
+    assert tsp.dllm_workspace_bytes(tsp.OP_SALIENCY, s, 128) == 0
+    assert tsp.dllm_workspace_bytes(tsp.OP_SELECT, s, 128) == 0
+    q = tsp.dllm_workspace_bytes(tsp.OP_QKV, s, 128)
+    f = tsp.dllm_workspace_bytes(tsp.OP_FFN, s, 128)
+    assert q >= 128 * 4096 * 2                       # normalised rows
+    assert f >= 128 * 4096 * 4 + 128 * 4096 * 2 + 128 * 12288 * 2
+    assert tsp.dllm_workspace_bytes(tsp.OP_QKV, s, 0) == 0
+    with pytest.raises(tsp.DllmError):
+        tsp.dllm_workspace_bytes(7, s, 128)
+    with pytest.raises(tsp.DllmError):
+        tsp.dllm_workspace_bytes(tsp.OP_QKV, s, 1025)  # m_cap > B*S
+
+
+def rc(fn, *args):
+    with pytest.raises(tsp.DllmError) as e:
+        fn(*args)
+    return e.value.status
+
+
+def test_saliency_validation():
+    s = llada()
+    f = tsp.dllm_saliency
+    assert rc(f, s, 0, 0.5, P, P, None, P) == tsp.DLLM_ERR_INVALID_ARG      # alpha>0, no logits
+    assert rc(f, s, 0, 0.5, None, None, P, P) == tsp.DLLM_ERR_INVALID_ARG   # alpha<1, no h
+    assert rc(f, s, 0, 1.5, P, P, P, P) == tsp.DLLM_ERR_INVALID_ARG         # alpha > 1
+    assert rc(f, s, 0, float("nan"), P, P, P, P) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(f, s, 3, 0.5, P, P, P, P) == tsp.DLLM_ERR_INVALID_ARG         # bad delta kind
+    assert rc(f, s, 0, 0.5, P, P, P, None) == tsp.DLLM_ERR_INVALID_ARG      # no score
+    assert rc(f, s, 0, 0.5, P, None, P, P) == tsp.DLLM_ERR_INVALID_ARG      # h_prev missing
+    assert rc(f, s, 0, 0.0, P, P, None, P, P) == tsp.DLLM_ERR_INVALID_ARG   # conf_out w/o logits
+    assert rc(f, s, 0, 0.5, P + 2, P, P, P) == tsp.DLLM_ERR_INVALID_ARG     # misaligned
+    bad = llada(); bad.V = 1001
+    assert rc(f, bad, 0, 0.5, P, P, P, P) == tsp.DLLM_ERR_UNSUPPORTED      # V % 8
+    bad = llada(); bad.B = 0
+    assert rc(f, bad, 0, 0.0, P, P, None, P) == tsp.DLLM_ERR_INVALID_ARG
+
+
+def test_select_validation():
+    s = llada()
+    f = tsp.dllm_select_compact
+    assert rc(f, s, tsp.SEL_TOPK, 0.0, -1, P, None, P, P) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(f, s, 5, 0.0, 1, P, None, P, P) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(f, s, tsp.SEL_THRESHOLD, float("nan"), 1, P, None, P, P) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(f, s, tsp.SEL_TOPK, 0.0, 1, None, None, P, P) == tsp.DLLM_ERR_INVALID_ARG
+    big = llada(S=tsp.MAX_SELECT_S + 1)
+    assert rc(f, big, tsp.SEL_TOPK, 0.0, 1, P, None, P, P) == tsp.DLLM_ERR_UNSUPPORTED
+
+
+def test_layer_call_validation():
+    s = llada()
+    q, a, ff = tsp.dllm_gather_qkv_scatter_kv, tsp.dllm_partial_attn, tsp.dllm_gather_ffn_scatter
+    ws = None
+    # NULL required pointer
+    assert rc(q, s, None, P, P, P, P, 128, P, P, P, ws) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(a, s, 0.1, P, P, P, P, None, 128, P, ws) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(ff, s, P, P, P, P, P, P, P, P, P, 128, None, ws) == tsp.DLLM_ERR_INVALID_ARG
+    # m_cap outside [0, B*S]
+    assert rc(q, s, P, P, P, P, P, -1, P, P, P, ws) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(q, s, P, P, P, P, P, 1025, P, P, P, ws) == tsp.DLLM_ERR_INVALID_ARG
+    # H % Hkv
+    bad = llada(); bad.Hkv = 5
+    assert rc(a, bad, 0.1, P, P, P, P, P, 128, P, ws) == tsp.DLLM_ERR_INVALID_ARG
+    # unsupported head width / model width
+    bad = llada(); bad.hd = 96
+    assert rc(a, bad, 0.1, P, P, P, P, P, 128, P, ws) == tsp.DLLM_ERR_UNSUPPORTED
+    bad = llada(); bad.d = 4000
+    assert rc(ff, bad, P, P, P, P, P, P, P, P, P, 128, P, ws) == tsp.DLLM_ERR_UNSUPPORTED
+    # non-finite scale, bad dtype, nonzero reserved field
+    assert rc(a, s, float("inf"), P, P, P, P, P, 128, P, ws) == tsp.DLLM_ERR_INVALID_ARG
+    bad = llada(); bad.dtype = 7
+    assert rc(q, bad, P, P, P, P, P, 128, P, P, P, ws) == tsp.DLLM_ERR_INVALID_ARG
+    bad = llada(); bad.reserved = 1
+    assert rc(q, bad, P, P, P, P, P, 128, P, P, P, ws) == tsp.DLLM_ERR_INVALID_ARG
+    # workspace too small (reported before any launch)
+    lib = tsp.library()
+    need = tsp.dllm_workspace_bytes(tsp.OP_QKV, s, 128)
+    st = lib.dllm_gather_qkv_scatter_kv(ctypes.byref(s), P, P, P, P, P, 128, P, P, P, P,
+                                        need - 1, None)
+    assert st == tsp.DLLM_ERR_WORKSPACE
+    need = tsp.dllm_workspace_bytes(tsp.OP_FFN, s, 128)
+    st = lib.dllm_gather_ffn_scatter(ctypes.byref(s), P, P, P, P, P, P, P, P, P, 128, P, P,
+                                     need - 1, None)
+    assert st == tsp.DLLM_ERR_WORKSPACE
+    need = tsp.dllm_workspace_bytes(tsp.OP_ATTN, s, 128)
+    assert need > 0  # batch 1, M = 128 splits the key range
+    st = lib.dllm_partial_attn(ctypes.byref(s), 0.1, P, P, P, P, P, 128, P, P, need - 1, None)
+    assert st == tsp.DLLM_ERR_WORKSPACE

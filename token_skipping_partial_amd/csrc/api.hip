@@ -1,0 +1,208 @@
+// C ABI of the token-skipping step library: host-side validation, workspace sizing, dispatch.
+// Every check runs before anything is enqueued; a non-OK status means no launch happened.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/dllm.h"
+#include "kernels.h"
+
+using namespace dllm;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool base_shape_ok(const dllm_shape* s) {
+  return s && s->B > 0 && s->S > 0 && s->d > 0 && (s->dtype == DLLM_F32 || s->dtype == DLLM_BF16) &&
+         s->reserved == 0 && (long)s->B * (long)s->S <= 0x7fffffffL;
+}
+
+// shape checks shared by the three layer calls; INVALID_ARG before UNSUPPORTED
+dllm_status layer_shape_status(const dllm_shape* s, int32_t m_cap) {
+  if (!base_shape_ok(s) || s->H <= 0 || s->Hkv <= 0 || s->hd <= 0 || s->F <= 0 ||
+      s->H % s->Hkv != 0 || m_cap < 0 || (long)m_cap > (long)s->B * s->S ||
+      !(s->rms_eps >= 0.f) || !isfinite(s->rms_eps))
+    return DLLM_ERR_INVALID_ARG;
+  if ((s->hd != 64 && s->hd != 128) || s->d % 64 != 0 || s->F % 64 != 0)
+    return DLLM_ERR_UNSUPPORTED;
+  return DLLM_OK;
+}
+
+ProjShape proj_shape(const dllm_shape* s, int32_t m_cap) {
+  ProjShape p;
+  p.B = s->B; p.S = s->S; p.d = s->d; p.H = s->H; p.Hkv = s->Hkv; p.hd = s->hd; p.F = s->F;
+  p.eps = s->rms_eps;
+  p.m_cap = m_cap;
+  return p;
+}
+
+dllm_status hip_status(hipError_t e) { return e == hipSuccess ? DLLM_OK : DLLM_ERR_HIP; }
+
+dllm_status ws_status(const void* ws, size_t have, size_t need) {
+  if (need == 0) return DLLM_OK;
+  if (have < need) return DLLM_ERR_WORKSPACE;
+  if (!ws || !aligned16(ws)) return DLLM_ERR_INVALID_ARG;
+  return DLLM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dllm_version(void) { return 100; }
+
+const char* dllm_status_string(int32_t status) {
+  switch (status) {
+    case DLLM_OK: return "DLLM_OK";
+    case DLLM_ERR_INVALID_ARG: return "DLLM_ERR_INVALID_ARG";
+    case DLLM_ERR_UNSUPPORTED: return "DLLM_ERR_UNSUPPORTED";
+    case DLLM_ERR_WORKSPACE: return "DLLM_ERR_WORKSPACE";
+    case DLLM_ERR_HIP: return "DLLM_ERR_HIP";
+    default: return "DLLM_ERR_UNKNOWN";
+  }
+}
+
+size_t dllm_workspace_bytes(int32_t op, const dllm_shape* shape, int32_t m_cap) {
+  switch (op) {
+    case DLLM_OP_SALIENCY:
+      return base_shape_ok(shape) ? 0 : (size_t)-1;
+    case DLLM_OP_SELECT:
+      return base_shape_ok(shape) ? 0 : (size_t)-1;
+    case DLLM_OP_QKV:
+    case DLLM_OP_ATTN:
+    case DLLM_OP_FFN: {
+      if (layer_shape_status(shape, m_cap) != DLLM_OK) return (size_t)-1;
+      const bool bf16 = shape->dtype == DLLM_BF16;
+      const ProjShape p = proj_shape(shape, m_cap);
+      if (op == DLLM_OP_QKV) return qkv_workspace_bytes(bf16, p);
+      if (op == DLLM_OP_ATTN) return attn_workspace_bytes(bf16, p);
+      return ffn_workspace_bytes(bf16, p);
+    }
+    default:
+      return (size_t)-1;
+  }
+}
+
+dllm_status dllm_saliency(const dllm_shape* shape, int32_t delta_kind, float alpha,
+                          const void* h_cur, const void* h_prev, const void* logits,
+                          float* score, float* conf_out, float* delta_out, void* stream) {
+  if (!base_shape_ok(shape) || !score || !(alpha >= 0.f && alpha <= 1.f) ||
+      delta_kind < DLLM_DELTA_L1N || delta_kind > DLLM_DELTA_L2R)
+    return DLLM_ERR_INVALID_ARG;
+  const bool has_h = h_cur != nullptr || h_prev != nullptr;
+  if (has_h && (!h_cur || !h_prev)) return DLLM_ERR_INVALID_ARG;
+  if (alpha != 1.f && !has_h) return DLLM_ERR_INVALID_ARG;
+  if (alpha != 0.f && !logits) return DLLM_ERR_INVALID_ARG;
+  if (conf_out && !logits) return DLLM_ERR_INVALID_ARG;
+  if (delta_out && !has_h) return DLLM_ERR_INVALID_ARG;
+  if (logits && shape->V <= 0) return DLLM_ERR_INVALID_ARG;
+  for (const void* p : {h_cur, h_prev, logits, (const void*)score, (const void*)conf_out,
+                        (const void*)delta_out})
+    if (p && ((uintptr_t)p & 3u)) return DLLM_ERR_INVALID_ARG;
+  for (const void* p : {h_cur, h_prev, logits})
+    if (p && !aligned16(p)) return DLLM_ERR_INVALID_ARG;
+  if (has_h && shape->d % 8 != 0) return DLLM_ERR_UNSUPPORTED;
+  if (logits && shape->V % 8 != 0) return DLLM_ERR_UNSUPPORTED;
+
+  SaliencyArgs a;
+  a.ntok = shape->B * shape->S;
+  a.d = shape->d;
+  a.V = (long)shape->V;
+  a.kind = delta_kind;
+  a.alpha = alpha;
+  a.h_cur = h_cur;
+  a.h_prev = h_prev;
+  // the vocabulary stream is skipped when neither the score nor an output needs it
+  a.logits = (alpha != 0.f || conf_out) ? logits : nullptr;
+  a.score = score;
+  a.conf_out = conf_out;
+  a.delta_out = delta_out;
+  return hip_status(launch_saliency(a, shape->dtype == DLLM_BF16, (hipStream_t)stream));
+}
+
+dllm_status dllm_select_compact(const dllm_shape* shape, int32_t mode, float tau, int32_t k,
+                                const float* score, const uint8_t* force, int32_t* sel_idx,
+                                int32_t* row_ptr, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!base_shape_ok(shape) || !score || !sel_idx || !row_ptr) return DLLM_ERR_INVALID_ARG;
+  if (mode == DLLM_SEL_TOPK) {
+    if (k < 0) return DLLM_ERR_INVALID_ARG;
+  } else if (mode == DLLM_SEL_THRESHOLD) {
+    if (isnan(tau)) return DLLM_ERR_INVALID_ARG;
+  } else {
+    return DLLM_ERR_INVALID_ARG;
+  }
+  if (((uintptr_t)score & 3u) || ((uintptr_t)sel_idx & 3u) || ((uintptr_t)row_ptr & 3u))
+    return DLLM_ERR_INVALID_ARG;
+  if (shape->S > DLLM_MAX_SELECT_S) return DLLM_ERR_UNSUPPORTED;
+  SelectArgs a;
+  a.B = shape->B;
+  a.S = shape->S;
+  a.mode = mode;
+  a.k = k;
+  a.tau = tau;
+  a.score = score;
+  a.force = force;
+  a.sel_idx = sel_idx;
+  a.row_ptr = row_ptr;
+  return hip_status(launch_select(a, (hipStream_t)stream));
+}
+
+dllm_status dllm_gather_qkv_scatter_kv(const dllm_shape* shape, const void* h_in,
+                                       const void* g_attn, const void* w_qkv,
+                                       const int32_t* sel_idx, const int32_t* row_ptr,
+                                       int32_t m_cap, void* q_sel, void* k_cache, void* v_cache,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  dllm_status st = layer_shape_status(shape, m_cap);
+  if (st != DLLM_OK) return st;
+  if (!h_in || !g_attn || !w_qkv || !sel_idx || !row_ptr || !q_sel || !k_cache || !v_cache)
+    return DLLM_ERR_INVALID_ARG;
+  for (const void* p : {h_in, g_attn, w_qkv, (const void*)q_sel, (const void*)k_cache,
+                        (const void*)v_cache})
+    if (!aligned16(p)) return DLLM_ERR_INVALID_ARG;
+  const bool bf16 = shape->dtype == DLLM_BF16;
+  const ProjShape p = proj_shape(shape, m_cap);
+  if ((st = ws_status(ws, ws_bytes, qkv_workspace_bytes(bf16, p))) != DLLM_OK) return st;
+  return hip_status(launch_qkv(bf16, p, h_in, g_attn, w_qkv, sel_idx, row_ptr, q_sel, k_cache,
+                               v_cache, ws, (hipStream_t)stream));
+}
+
+dllm_status dllm_partial_attn(const dllm_shape* shape, float scale, const void* q_sel,
+                              const void* k_cache, const void* v_cache, const int32_t* sel_idx,
+                              const int32_t* row_ptr, int32_t m_cap, void* o_sel, void* ws,
+                              size_t ws_bytes, void* stream) {
+  dllm_status st = layer_shape_status(shape, m_cap);
+  if (st != DLLM_OK) return st;
+  if (!q_sel || !k_cache || !v_cache || !sel_idx || !row_ptr || !o_sel || !isfinite(scale))
+    return DLLM_ERR_INVALID_ARG;
+  for (const void* p : {q_sel, k_cache, v_cache, (const void*)o_sel})
+    if (!aligned16(p)) return DLLM_ERR_INVALID_ARG;
+  const bool bf16 = shape->dtype == DLLM_BF16;
+  const ProjShape p = proj_shape(shape, m_cap);
+  if ((st = ws_status(ws, ws_bytes, attn_workspace_bytes(bf16, p))) != DLLM_OK) return st;
+  return hip_status(launch_attn(bf16, p, scale, q_sel, k_cache, v_cache, sel_idx, row_ptr, o_sel,
+                                ws, (hipStream_t)stream));
+}
+
+dllm_status dllm_gather_ffn_scatter(const dllm_shape* shape, const void* h_in, const void* o_sel,
+                                    const void* w_o, const void* g_ffn, const void* w_gate,
+                                    const void* w_up, const void* w_down,
+                                    const int32_t* sel_idx, const int32_t* row_ptr,
+                                    int32_t m_cap, void* h_out, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  dllm_status st = layer_shape_status(shape, m_cap);
+  if (st != DLLM_OK) return st;
+  if (!h_in || !o_sel || !w_o || !g_ffn || !w_gate || !w_up || !w_down || !sel_idx ||
+      !row_ptr || !h_out)
+    return DLLM_ERR_INVALID_ARG;
+  for (const void* p : {h_in, o_sel, w_o, g_ffn, w_gate, w_up, w_down, (const void*)h_out})
+    if (!aligned16(p)) return DLLM_ERR_INVALID_ARG;
+  const bool bf16 = shape->dtype == DLLM_BF16;
+  const ProjShape p = proj_shape(shape, m_cap);
+  if ((st = ws_status(ws, ws_bytes, ffn_workspace_bytes(bf16, p))) != DLLM_OK) return st;
+  return hip_status(launch_ffn(bf16, p, h_in, o_sel, w_o, g_ffn, w_gate, w_up, w_down, sel_idx,
+                               row_ptr, h_out, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels. Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dllm {
+
+struct SaliencyArgs {
+  int ntok, d;
+  long V;
+  int kind;
+  float alpha;
+  const void* h_cur;
+  const void* h_prev;
+  const void* logits;  // NULL when the confidence term is not needed
+  float* score;
+  float* conf_out;
+  float* delta_out;
+};
+hipError_t launch_saliency(const SaliencyArgs& a, bool bf16, hipStream_t st);
+
+struct SelectArgs {
+  int B, S, mode, k;
+  float tau;
+  const float* score;
+  const uint8_t* force;
+  int32_t* sel_idx;
+  int32_t* row_ptr;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- gathered projections
+struct ProjShape {
+  int B, S, d, H, Hkv, hd, F;
+  float eps;
+  int m_cap;
+};
+
+// launch plan of one GEMM: tile height, number of K splits
+struct GemmPlan {
+  int bm;      // 64 or 128 rows per tile (bf16); fp32 path uses its own tiles
+  int splits;  // K partitions reduced in a second pass (1 = fused epilogue)
+};
+GemmPlan plan_gemm(bool bf16, int m_cap, int N, int K, bool splittable);
+size_t gemm_partials_bytes(const GemmPlan& p, int m_cap, int N);
+
+size_t qkv_workspace_bytes(bool bf16, const ProjShape& s);
+size_t ffn_workspace_bytes(bool bf16, const ProjShape& s);
+
+hipError_t launch_qkv(bool bf16, const ProjShape& s, const void* h_in, const void* g_attn,
+                      const void* w_qkv, const int32_t* sel_idx, const int32_t* row_ptr,
+                      void* q_sel, void* k_cache, void* v_cache, void* ws, hipStream_t st);
+
+hipError_t launch_ffn(bool bf16, const ProjShape& s, const void* h_in, const void* o_sel,
+                      const void* w_o, const void* g_ffn, const void* w_gate, const void* w_up,
+                      const void* w_down, const int32_t* sel_idx, const int32_t* row_ptr,
+                      void* h_out, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------- partial attention
+struct AttnPlan {
+  int nsplit;  // key-range partitions merged by log-sum-exp in a second pass
+};
+AttnPlan plan_attn(bool bf16, const ProjShape& s);
+size_t attn_workspace_bytes(bool bf16, const ProjShape& s);
+
+hipError_t launch_attn(bool bf16, const ProjShape& s, float scale, const void* q_sel,
+                       const void* k_cache, const void* v_cache, const int32_t* sel_idx,
+                       const int32_t* row_ptr, void* o_sel, void* ws, hipStream_t st);
+
+}  // namespace dllm
