@@ -1,0 +1,248 @@
+"""Benchmark of the token-skipping denoising step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload llada_layer]
+
+Default workload: one LLaDA-8B-shaped layer (bf16, B=1, S=1024, d=4096, 32 heads x 128,
+FFN 12288, vocabulary 126464). A step is the whole hot path on one batch:
+saliency (alpha = 0.5, L1-normalised delta + max-softmax confidence) -> top-128 selection ->
+gathered QKV + K/V scatter -> partial attention -> gathered FFN + hidden scatter.
+16 independent sets of weights/logits/hidden/caches rotate from step to step so that no set is
+still resident in the 256 MB last-level cache; every input is in HBM before the timed region.
+
+Metric: selected-token layer-steps per second (selected rows x selected layers per second).
+Rank 0 prints one JSON line with the step rate, the roofline of the dominant kernel (HIP events
+around its launch inside the timed region), the partial-attention HBM rate, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix peak, published
+METRIC = "selected-token layer-steps/sec at 8B shape; partial-attn HBM GB/s % peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="llada_layer", choices=["llada_layer"])
+    p.add_argument("--sets", type=int, default=16, help="rotated input/weight sets")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="budget of the CPU oracle sample (0 = skip)")
+    return p.parse_args()
+
+
+def kernel_traffic(kernel: str, source: str):
+    """Measured HBM bytes per launch from profiles/traffic.json, or None when the kernel's
+    source has changed since the counters were taken (hash mismatch) or none were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    with open(os.path.join(ROOT, source), "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the token-skipping step on a single "
+              "MI355X (no collectives). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import token_skipping_partial_amd as tsp  # raises if libdllm.so is not built
+    from synth import workloads as W
+    from token_skipping_partial_amd.step import (LayerScratch, LayerWeights, SelectConfig,
+                                                 SingleLayerStep, all_rows, selected_layer)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    dims = W.LLADA_LAYER
+    k_sel = W.LLADA_TOPK
+    shape = tsp.Shape(B=dims.B, S=dims.S, d=dims.d, H=dims.H, Hkv=dims.Hkv, hd=dims.hd,
+                      F=dims.F, dtype="bf16", V=dims.V)
+    print(f"[bench] building {args.sets} input sets of {shape}", file=sys.stderr, flush=True)
+
+    sets = []
+    fill = LayerScratch(shape, dims.B * dims.S, dev)
+    sel_all, rp_all = all_rows(shape, dev)
+    for i in range(args.sets):
+        h_prev, h_cur, _, logits, w = W.layer_inputs(dims, W.LLADA_LARGE, seed=9000 + i,
+                                                     device=dev)
+        wd = LayerWeights.from_dict(w, dev)
+        kc = torch.zeros(dims.B, dims.Hkv, dims.S, dims.hd, dtype=dims.dtype, device=dev)
+        vc = torch.zeros_like(kc)
+        h_out = torch.zeros(dims.B, dims.S, dims.d, dtype=dims.dtype, device=dev)
+        # step t-1 state: the layer on every token of h_prev (untimed)
+        selected_layer(shape, wd, h_prev, kc, vc, h_out, sel_all, rp_all, fill)
+        sets.append((wd, h_prev, h_cur, logits, kc, vc, h_out))
+    del fill
+    torch.cuda.synchronize()
+
+    step = SingleLayerStep(shape, SelectConfig(mode=tsp.SEL_TOPK, k=k_sel, alpha=0.5), k_sel, dev)
+    stream = torch.cuda.current_stream()
+
+    def run(i, ev=None):
+        wd, h_prev, h_cur, logits, kc, vc, h_out = sets[i % len(sets)]
+        sc = step.scratch
+        if ev is not None:
+            ev[0].record(stream)
+        tsp.dllm_saliency(shape, tsp.DELTA_L1N, 0.5, h_cur, h_prev, logits, step.score)
+        if ev is not None:
+            ev[1].record(stream)
+        tsp.dllm_select_compact(shape, tsp.SEL_TOPK, 0.0, k_sel, step.score, None, step.sel_idx,
+                                step.row_ptr)
+        if ev is not None:
+            ev[2].record(stream)
+        tsp.dllm_gather_qkv_scatter_kv(shape, h_cur, wd.g_attn, wd.w_qkv, step.sel_idx,
+                                       step.row_ptr, k_sel, sc.q_sel, kc, vc, sc.ws_qkv)
+        if ev is not None:
+            ev[3].record(stream)
+        tsp.dllm_partial_attn(shape, 1.0 / math.sqrt(dims.hd), sc.q_sel, kc, vc, step.sel_idx,
+                              step.row_ptr, k_sel, sc.o_sel, sc.ws_attn)
+        if ev is not None:
+            ev[4].record(stream)
+        tsp.dllm_gather_ffn_scatter(shape, h_cur, sc.o_sel, wd.w_o, wd.g_ffn, wd.w_gate, wd.w_up,
+                                    wd.w_down, step.sel_idx, step.row_ptr, k_sel, h_out, sc.ws_ffn)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        run(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    M = int(step.row_ptr[-1].item())
+    value = M * args.steps / (total_ms / 1e3)
+
+    names = ["saliency", "select_compact", "gather_qkv_scatter_kv", "partial_attn",
+             "gather_ffn_scatter"]
+    per_call = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+                for j, n in enumerate(names)}
+
+    # algorithmic bytes / flops per launch (what the method must move or compute)
+    b = 2
+    ntok = dims.B * dims.S
+    nq, nkv = dims.H * dims.hd, dims.Hkv * dims.hd
+    sal_bytes = ntok * (2 * dims.d * b + dims.V * b + 4)
+    attn_bytes = (M * nq * b * 2 + 2 * dims.B * dims.S * nkv * b + M * 4 + (dims.B + 1) * 4)
+    qkv_bytes = (nq + 2 * nkv) * dims.d * b + M * (dims.d * b + (nq + 2 * nkv) * b) + dims.d * b
+    ffn_bytes = (dims.d * nq + 3 * dims.F * dims.d) * b + M * (nq * b + 2 * dims.d * b) + dims.d * b
+    qkv_flops = 2.0 * M * (nq + 2 * nkv) * dims.d
+    ffn_flops = 2.0 * M * (dims.d * nq + 3 * dims.F * dims.d)
+    attn_flops = 4.0 * M * dims.S * nq
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9  # noqa: E731
+
+    kernels = {
+        "saliency": {"ms": per_call["saliency"], "bytes": sal_bytes,
+                     "GB/s": gbs(sal_bytes, per_call["saliency"])},
+        "select_compact": {"ms": per_call["select_compact"]},
+        "gather_qkv_scatter_kv": {"ms": per_call["gather_qkv_scatter_kv"], "bytes": qkv_bytes,
+                                  "GB/s": gbs(qkv_bytes, per_call["gather_qkv_scatter_kv"]),
+                                  "TFLOP/s": qkv_flops / per_call["gather_qkv_scatter_kv"] / 1e9},
+        "partial_attn": {"ms": per_call["partial_attn"], "bytes": attn_bytes,
+                         "GB/s": gbs(attn_bytes, per_call["partial_attn"]),
+                         "TFLOP/s": attn_flops / per_call["partial_attn"] / 1e9},
+        "gather_ffn_scatter": {"ms": per_call["gather_ffn_scatter"], "bytes": ffn_bytes,
+                               "GB/s": gbs(ffn_bytes, per_call["gather_ffn_scatter"]),
+                               "TFLOP/s": ffn_flops / per_call["gather_ffn_scatter"] / 1e9},
+    }
+    sal_gbs = kernels["saliency"]["GB/s"]
+    roofline = {"kernel": "saliency_logits_kernel (dllm_saliency: one launch per call)",
+                "bound": "hbm", "achieved": round(sal_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(sal_gbs / HBM_PEAK_GBS, 4),
+                "traffic": kernel_traffic("saliency_logits_kernel",
+                                          "token_skipping_partial_amd/csrc/saliency.hip")}
+    attn_gbs = kernels["partial_attn"]["GB/s"]
+    partial_attn = {"achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                    "launches": "attention kernel + split-key merge kernel"}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(sets[0], dims, k_sel, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "selected-token layer-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: hidden N(0,1); 15% of tokens + N(0,0.5^2), the rest + N(0,(1e-3)^2); "
+                "logits N(0,3^2); random-init weights N(0,0.02^2)",
+        "config": {"workload": "llada_layer: one LLaDA-8B-shaped layer step, B=1, S=1024, "
+                               "d=4096, 32x128 MHA, FFN 12288, V=126464, alpha=0.5, top-128",
+                   "selected_per_step": M, "rotated_sets": args.sets},
+        "roofline": roofline,
+        "partial_attn": partial_attn,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                        for kk, vv in v.items()} for k, v in kernels.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(one_set, dims, k_sel, budget_s):
+    """The CPU oracle on the same workload: whole steps (saliency over every token and the full
+    vocabulary, selection, then the layer on the selected rows) until the budget is used."""
+    import numpy as np
+
+    import oracle as O
+
+    wd, h_prev, h_cur, logits, kc, vc, h_out = one_set
+    dec = lambda t: O.decode_bf16(t.detach().cpu().contiguous().view(torch.uint16).numpy())  # noqa
+    hp, hc, lg = dec(h_prev[0]), dec(h_cur[0]), dec(logits[0])
+    w = {n: dec(getattr(wd, n)) for n in ("g_attn", "w_qkv", "w_o", "g_ffn", "w_gate", "w_up",
+                                            "w_down")}
+    k0, v0, y0 = dec(kc), dec(vc), dec(h_out)
+    scale = 1.0 / math.sqrt(dims.hd)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        score, _, _ = O.saliency(hc, hp, lg, 0.5)
+        sel, rp = O.select_compact(score.reshape(1, -1), None, O.SEL_TOPK, k=k_sel)
+        O.selected_layer(hc[None], w, sel, rp, k0, v0, y0, dims.H, dims.Hkv, dims.hd, 1e-5, scale)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 200:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max(i.get("num_threads", 1) for i in threadpool_info())
+    except Exception:
+        blas_threads = os.cpu_count()
+    return {"value": round(k_sel * steps / el, 2), "unit": "selected-token layer-steps/s",
+            "cores": blas_threads, "kind": "oracle",
+            "sample": f"{steps} whole oracle steps of the same workload (set 0), {el:.1f} s; "
+                      f"float64 numpy, BLAS products on {blas_threads} threads, the rest on one"}
+
+
+if __name__ == "__main__":
+    main()
