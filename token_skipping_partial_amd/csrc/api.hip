@@ -3,7 +3,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "../../include/dllm.h"
+#include "dllm.h"
 #include "kernels.h"
 
 using namespace dllm;

@@ -131,11 +131,27 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const Tin* in, const 
 }
 
 // =========================================================================================
-// bf16 matrix-core GEMM
+// bf16 matrix-core GEMM fed by a direct-to-LDS load ring
 // =========================================================================================
-constexpr int kBN = 128;      // weight rows per tile (SwiGLU: 64 gate + 64 up rows)
-constexpr int kBK = 64;       // K per step
-constexpr int kPitch = 72;    // LDS row pitch in bf16 (64 + 8 pad = 144 bytes)
+// Per K step of 64 a workgroup stages [BM rows of X ; BN rows of W] x 128 bytes in one slot of
+// an ST-slot LDS ring. global_load_lds_dwordx4 moves 64 lanes x 16 B (8 rows) per wave
+// instruction from global memory straight into 1 KB of LDS, without passing through registers,
+// so ST - 1 K steps stay in flight while the matrix cores work on the oldest slot. One
+// s_barrier per K step: the slot refilled at step kt is the one every wave finished at kt - 1.
+// Inside a 128-byte row the 16-byte chunk c is stored at c ^ g(row), g(r) = (r & 7) ^ (r >> 3 & 1),
+// so the 16 lanes that read one MFMA fragment (16 rows, one chunk) hit distinct bank groups.
+//
+// Tile shapes (host plan): at M <= 128 the products stream weights from HBM, and the plan picks
+// BN so that about 256 workgroups each own a disjoint weight slab (QKV: BN = 48 -> 256 slabs of
+// the 12288 rows; gate/up: 48 + 48 rows); 4 waves split the M rows, so every X row is read from
+// LDS once. Narrow N (4096) uses BN = 64 and a few K splits. At larger M, 128 x 128 tiles with
+// 2 x 2 waves.
+constexpr int kBK = 64;
+
+// ring slots that fit in the 160 KB of LDS a workgroup may use, capped at `want`
+constexpr int ring_slots(int bm, int bn, int bk, int want) {
+  return (160 * 1024) / ((bm + bn) * bk * 2) < want ? (160 * 1024) / ((bm + bn) * bk * 2) : want;
+}
 
 struct GemmArgs {
   const uint16_t* X;   // [m_cap, K] compact activations
@@ -147,146 +163,206 @@ struct GemmArgs {
   float* partial;      // [splits, m_cap, N] when split, else NULL
 };
 
-template <int BM>
-struct TileRegs {
-  uint4 a[BM / 32];
-  uint4 w[4];
-};
+// 16-byte chunk swizzle for rows of 128 bytes (8 chunks) or 256 bytes (16 chunks): the 16 rows
+// read by one MFMA fragment land on distinct bank groups for either bank width.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return r & 15;
+}
 
-template <int BM, bool SWIGLU>
-__device__ __forceinline__ void load_tile(const GemmArgs& g, int m0, int n0, int M, int k0,
-                                          TileRegs<BM>& r) {
-  const int t = threadIdx.x;
-  const int col = (t & 7) * 8;
-#pragma unroll
-  for (int i = 0; i < BM / 32; ++i) {
-    const int row = (t >> 3) + 32 * i;
-    const int m = m0 + row;
-    r.a[i] = (m < M) ? *reinterpret_cast<const uint4*>(g.X + (size_t)m * g.K + k0 + col)
-                     : make_uint4(0, 0, 0, 0);
+// wait until at most N vector-memory operations of this wave are outstanding (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// workgroup barrier without the release/acquire fences of __syncthreads(): the fence would make
+// the compiler wait for every load in flight, which defeats the ring
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int PB, int A>
+__device__ __forceinline__ void wait_batches(int ahead) {  // wait until <= ahead*PB ops pending
+  if constexpr (A == 0) {
+    wait_vm<0>();
+  } else {
+    if (ahead >= A)
+      wait_vm<A * PB>();
+    else
+      wait_batches<PB, A - 1>(ahead);
   }
+}
+
+// One ring slot = [BM rows of X ; BN rows of W] x BK columns (BK * 2 bytes per row).
+template <int BM, int BN, int BK, int NW, bool SWIGLU>
+__device__ __forceinline__ void issue_stage(const GemmArgs& g, char* slot, int m0, int n0, int M,
+                                            int k0, int wave, int lane) {
+  constexpr int RB = BK * 2;         // bytes per row
+  constexpr int CPR = RB / 16;       // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;     // rows per wave instruction
+  constexpr int I = (BM + BN) / RPI; // wave instructions per slot
+  constexpr int PER = (I + NW - 1) / NW;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (t >> 3) + 32 * i;
-    const uint16_t* src;
-    int n;
-    if (SWIGLU) {
-      n = n0 + (row & 63);
-      src = (row < 64) ? g.W : g.W2;
-    } else {
-      n = n0 + row;
-      src = g.W;
+  for (int i = 0; i < PER; ++i) {
+    const int j = wave + NW * i;
+    if (j < I) {
+      const int row = RPI * j + lane / CPR;
+      const int c = (lane % CPR) ^ swz<CPR>(row);
+      const uint16_t* src;
+      if (row < BM) {
+        // rows past M repeat row M-1: their products land in rows that are never stored
+        src = g.X + (size_t)min(m0 + row, M - 1) * g.K;
+      } else {
+        const int r = row - BM;
+        if constexpr (SWIGLU) {
+          const int n = min(n0 + (r % (BN / 2)), g.N - 1);
+          src = ((r < BN / 2) ? g.W : g.W2) + (size_t)n * g.K;
+        } else {
+          src = g.W + (size_t)min(n0 + r, g.N - 1) * g.K;
+        }
+      }
+      __builtin_amdgcn_global_load_lds(src + k0 + 8 * c, (lds_void*)(slot + j * 1024), 16, 0, 0);
     }
-    r.w[i] = (n < g.N) ? *reinterpret_cast<const uint4*>(src + (size_t)n * g.K + k0 + col)
-                       : make_uint4(0, 0, 0, 0);
   }
 }
 
-template <int BM>
-__device__ __forceinline__ void store_tile(uint16_t* sA, uint16_t* sW, const TileRegs<BM>& r) {
-  const int t = threadIdx.x;
-  const int col = (t & 7) * 8;
-#pragma unroll
-  for (int i = 0; i < BM / 32; ++i)
-    *reinterpret_cast<uint4*>(sA + ((t >> 3) + 32 * i) * kPitch + col) = r.a[i];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint4*>(sW + ((t >> 3) + 32 * i) * kPitch + col) = r.w[i];
+// first W row (within the W part of the slot) of the wave's n-block j
+template <int BN, int WN, int NB, bool SWIGLU>
+__device__ __forceinline__ int wrow(int wn, int j) {
+  if constexpr (SWIGLU) {
+    constexpr int HW = BN / 2 / WN;  // gate rows per wave
+    return (j < NB / 2) ? wn * HW + 16 * j : BN / 2 + wn * HW + 16 * (j - NB / 2);
+  } else {
+    return wn * (BN / WN) + 16 * j;
+  }
 }
 
-// LDS row of the wave's n-block nb (0..3). SwiGLU pairs gate block nb with up block nb + 2.
-template <bool SWIGLU>
-__device__ __forceinline__ int wrow_base(int wn, int nb) {
-  if (SWIGLU) return (nb < 2) ? (32 * wn + 16 * nb) : (64 + 32 * wn + 16 * (nb - 2));
-  return 64 * wn + 16 * nb;
+template <int BK>
+__device__ __forceinline__ bf16x8 frag(const char* slot, int row, int chunk) {
+  constexpr int RB = BK * 2;
+  return *reinterpret_cast<const bf16x8*>(slot + row * RB + ((chunk ^ swz<RB / 16>(row)) << 4));
 }
 
-template <int BM, bool SWIGLU, class Epi>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, Epi epi) {
-  constexpr int MB = BM / 32;  // 16-row m-blocks per wave (2 waves along m)
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[kBN * kPitch];
+// BM x BN tile, BK columns per ring slot, ST slots, NW waves as WM x WN.
+template <int BM, int BN, int BK, int WM, int WN, int ST, bool SWIGLU, class Epi>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g, Epi epi) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MB = WTM / 16, NB = WTN / 16;
+  constexpr int SLOT = (BM + BN) * BK * 2;
+  constexpr int NMIN = (BM + BN) * BK * 2 / 1024 / NW;  // DMA instructions per wave per slot (lower bound)
+  static_assert(MB >= 1 && NB >= 1 && (!SWIGLU || NB % 2 == 0), "tile");
+  static_assert(ST >= 3 && (ST - 2) * NMIN < 64 && NMIN >= 1, "ring depth");
+  __shared__ __attribute__((aligned(1024))) char ring[ST * SLOT];
 
   const int M = live_rows(g.row_ptr, g.B, g.m_cap);
   const int m0 = blockIdx.y * BM;
   if (m0 >= M) return;
-  const int n0 = blockIdx.x * (SWIGLU ? kBN / 2 : kBN);
+  const int n0 = blockIdx.x * (SWIGLU ? BN / 2 : BN);
   const int kb = blockIdx.z * g.kchunk;
-  const int ke = min(g.K, kb + g.kchunk);
+  const int nk = (min(g.K, kb + g.kchunk) - kb) / BK;  // >= 1 by the plan
+  // Each workgroup starts its K walk at a different slot: workgroups running side by side then
+  // read different column offsets of their weight rows instead of the same offset of rows a
+  // power-of-two stride apart. The order is a fixed function of the tile (deterministic).
+  const int rot = (int)((blockIdx.x * 37u + blockIdx.y * 11u) % (unsigned)nk);
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 15, lc = lane >> 4;
 
-  f32x4 acc[MB][4];
+  f32x4 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  TileRegs<BM> regs;
-  if (kb < ke) {  // a K split never starts past K (see plan_gemm), kept as a bound check
-    load_tile<BM, SWIGLU>(g, m0, n0, M, kb, regs);
-    store_tile<BM>(sA, sW, regs);
-  }
-  __syncthreads();
-
-  for (int k0 = kb; k0 < ke; k0 += kBK) {
-    const bool more = k0 + kBK < ke;
-    if (more) load_tile<BM, SWIGLU>(g, m0, n0, M, k0 + kBK, regs);
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      bf16x8 bx[MB], aw[4];
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nk)
+      issue_stage<BM, BN, BK, NW, SWIGLU>(g, ring + s * SLOT, m0, n0, M,
+                                          kb + ((s + rot) % nk) * BK, wave, lane);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_batches<NMIN, ST - 2>(nk - 1 - kt);  // slots issued after slot kt: min(ST-2, nk-1-kt)
+    wg_barrier();
+    if (kt + ST - 1 < nk)
+      issue_stage<BM, BN, BK, NW, SWIGLU>(g, ring + ((kt + ST - 1) % ST) * SLOT, m0, n0, M,
+                                          kb + ((kt + ST - 1 + rot) % nk) * BK, wave, lane);
+    const char* slot = ring + (kt % ST) * SLOT;
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      bf16x8 xf[MB], wf[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) xf[i] = frag<BK>(slot, wm * WTM + 16 * i + lr, 4 * kk + lc);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        wf[j] = frag<BK>(slot, BM + wrow<BN, WN, NB, SWIGLU>(wn, j) + lr, 4 * kk + lc);
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        bx[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * (BM / 2) + 16 * i + lr) * kPitch +
-                                                 kk + lk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        aw[j] = *reinterpret_cast<const bf16x8*>(sW + (wrow_base<SWIGLU>(wn, j) + lr) * kPitch +
-                                                 kk + lk);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[j], bx[i], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      __syncthreads();
-      store_tile<BM>(sA, sW, regs);
-      __syncthreads();
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
     }
   }
 
-  // acc[i][j][r] = C[m = wm*BM/2 + 16 i + lr][n = (n-block j row base) + 4*(lane/16) + r]
-  const int nq = 4 * (lane >> 4);
+  // acc[i][j][r] = C[m = m0 + wm WTM + 16 i + lr][n = n0 + (n-block j) + 4 lc + r]
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    const int m = m0 + wm * (BM / 2) + 16 * i + lr;
+    const int m = m0 + wm * WTM + 16 * i + lr;
     if (m >= M) continue;
     if constexpr (SWIGLU) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + 32 * wn + 16 * j + nq;
+      for (int j = 0; j < NB / 2; ++j) {
+        const int n = n0 + wrow<BN, WN, NB, true>(wn, j) + 4 * lc;
+        if (n >= g.N) continue;
         const float gv[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-        const float uv[4] = {acc[i][j + 2][0], acc[i][j + 2][1], acc[i][j + 2][2],
-                             acc[i][j + 2][3]};
-        epi(m, n, gv, uv);
+        const float uv[4] = {acc[i][j + NB / 2][0], acc[i][j + NB / 2][1],
+                             acc[i][j + NB / 2][2], acc[i][j + NB / 2][3]};
+        if (g.partial) {  // [split][row][gate 0..N | up N..2N]
+          float* pr = g.partial + ((size_t)blockIdx.z * g.m_cap + m) * (2 * (size_t)g.N);
+          Elem<float>::store4(pr + n, gv);
+          Elem<float>::store4(pr + g.N + n, uv);
+        } else {
+          epi(m, n, gv, uv);
+        }
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 64 * wn + 16 * j + nq;
+      for (int j = 0; j < NB; ++j) {
+        const int n = n0 + wrow<BN, WN, NB, false>(wn, j) + 4 * lc;
         if (n >= g.N) continue;
         const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-        if (g.partial) {
+        if (g.partial)
           Elem<float>::store4(g.partial + ((size_t)blockIdx.z * g.m_cap + m) * g.N + n, v);
-        } else {
+        else
           epi(m, n, v);
-        }
       }
     }
   }
+}
+
+// fixed-order sum of the K-split gate and up partials, then SiLU(gate) * up
+template <class Epi>
+__global__ __launch_bounds__(256) void splitk_swiglu_kernel(const float* partial, int splits,
+                                                            int N, const int32_t* row_ptr, int B,
+                                                            int m_cap, Epi epi) {
+  const int M = live_rows(row_ptr, B, m_cap);
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int groups = N / 4;
+  const int m = (int)(idx / groups);
+  if (m >= M) return;
+  const int n = (int)(idx - (size_t)m * groups) * 4;
+  float gv[4] = {0.f, 0.f, 0.f, 0.f}, uv[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < splits; ++z) {
+    const float* pr = partial + ((size_t)z * m_cap + m) * (2 * (size_t)N);
+    float a[4], b[4];
+    Elem<float>::load4(pr + n, a);
+    Elem<float>::load4(pr + N + n, b);
+    for (int e = 0; e < 4; ++e) { gv[e] += a[e]; uv[e] += b[e]; }
+  }
+  epi(m, n, gv, uv);
 }
 
 // fixed-order sum of the K-split partials, then the epilogue
@@ -391,15 +467,37 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF32 g, Epi epi) {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
-GemmPlan plan_gemm(bool bf16, int m_cap, int N, int K, bool splittable) {
-  GemmPlan p{64, 1};
+// Weight-streaming plans (M <= 128). Every tile covers all selected rows, so each workgroup
+// re-reads the K-slice of X it needs next to its weight slab; one workgroup per CU (about 256
+// tiles) streams disjoint slabs. Measured on MI355X at the LLaDA-8B layer shape (M = 128), the
+// fastest of the tile widths / K splits tried were:
+//   wide output (QKV, N = 12288): 48-row slabs (256 tiles), no split;
+//   narrow output (W_o, W_down, N = 4096): 64-row slabs, 4 K splits;  gate/up: 48 + 48 rows.
+// Wider slabs with more K splits move fewer bytes per CU but pay the partial round trip.
+GemmPlan plan_gemm(bool bf16, int m_cap, int N, int K, bool swiglu) {
+  GemmPlan p{64, 64, 64, 4, 1, 4, 1};
   if (!bf16) return p;
-  p.bm = m_cap <= 64 ? 64 : 128;
-  const long tiles = (long)cdiv(N, kBN) * cdiv(m_cap, p.bm);
-  if (splittable) {
-    // fill the 256 compute units (about two tiles each) while every split keeps >= 8 K steps
-    while (tiles * p.splits < 512 && K / (p.splits * 2) >= 8 * kBK && p.splits < 8) p.splits *= 2;
+  if (m_cap > 128) {
+    p = GemmPlan{128, 128, 64, 2, 2, 3, 1};
+    const long tiles = (long)cdiv(N, swiglu ? 64 : 128) * cdiv(m_cap, 128);
+    if (!swiglu)
+      while (tiles * p.splits < 256 && K / (p.splits * 2) >= 512 && p.splits < 8) p.splits *= 2;
+    return p;
   }
+  const int bm = m_cap <= 64 ? 64 : 128;
+  const int wm = bm / 32;  // waves of 32 rows
+  if (swiglu) {
+    p = GemmPlan{bm, 96, 64, wm, 1, 0, 1};
+  } else if (cdiv(N, 48) >= 224) {
+    p = GemmPlan{bm, 48, 64, wm, 1, 0, 1};
+  } else {
+    p = GemmPlan{bm, 64, 64, wm, 1, 0, 1};
+    const long tiles = cdiv(N, 64);
+    while (tiles * p.splits < 224 && K % (p.splits * 2 * 64) == 0 && K / (p.splits * 2) >= 512 &&
+           p.splits < 8)
+      p.splits *= 2;
+  }
+  p.st = ring_slots(p.bm, p.bn, p.bk, 4);
   return p;
 }
 
@@ -407,51 +505,79 @@ size_t gemm_partials_bytes(const GemmPlan& p, int m_cap, int N) {
   return p.splits > 1 ? (size_t)p.splits * m_cap * N * sizeof(float) : 0;
 }
 
-static int kchunk_of(const GemmPlan& p, int K) {
-  return cdiv(cdiv(K, p.splits), kBK) * kBK;
-}
+static int kchunk_of(const GemmPlan& p, int K) { return cdiv(cdiv(K, p.splits), p.bk) * p.bk; }
 
 size_t qkv_workspace_bytes(bool bf16, const ProjShape& s) {
   const int N = (s.H + 2 * s.Hkv) * s.hd;
   const size_t es = bf16 ? 2 : 4;
-  GemmPlan p = plan_gemm(bf16, s.m_cap, N, s.d, true);
+  GemmPlan p = plan_gemm(bf16, s.m_cap, N, s.d, false);
   return align256((size_t)s.m_cap * s.d * es) + align256(gemm_partials_bytes(p, s.m_cap, N));
 }
 
 size_t ffn_workspace_bytes(bool bf16, const ProjShape& s) {
   const size_t es = bf16 ? 2 : 4;
   const int Nq = s.H * s.hd;
-  GemmPlan po = plan_gemm(bf16, s.m_cap, s.d, Nq, true);
-  GemmPlan pd = plan_gemm(bf16, s.m_cap, s.d, s.F, true);
+  GemmPlan po = plan_gemm(bf16, s.m_cap, s.d, Nq, false);
+  GemmPlan pg = plan_gemm(bf16, s.m_cap, s.F, s.d, true);
+  GemmPlan pd = plan_gemm(bf16, s.m_cap, s.d, s.F, false);
   size_t part = gemm_partials_bytes(po, s.m_cap, s.d);
-  size_t part2 = gemm_partials_bytes(pd, s.m_cap, s.d);
-  if (part2 > part) part = part2;
+  const size_t part_g = gemm_partials_bytes(pg, s.m_cap, 2 * s.F);
+  const size_t part_d = gemm_partials_bytes(pd, s.m_cap, s.d);
+  if (part_g > part) part = part_g;
+  if (part_d > part) part = part_d;
   return align256((size_t)s.m_cap * s.d * 4) + align256((size_t)s.m_cap * s.d * es) +
          align256((size_t)s.m_cap * s.F * es) + align256(part);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int ST, bool SWIGLU, class Epi>
+static bool launch_if(const GemmPlan& p, const GemmArgs& g, dim3 grid, Epi epi, hipStream_t st) {
+  if constexpr (ST < 3) {  // shape does not fit a 3-slot ring in LDS; never planned
+    return false;
+  } else {
+    if (p.bm != BM || p.bn != BN || p.bk != BK || p.wm != WM || p.wn != WN || p.st != ST)
+      return false;
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, ST, SWIGLU, Epi>), grid,
+                       dim3(64 * WM * WN), 0, st, g, epi);
+    return true;
+  }
 }
 
 template <bool SWIGLU, class Epi>
 static hipError_t run_gemm_bf16(const GemmPlan& p, const uint16_t* X, const uint16_t* W,
                                 const uint16_t* W2, int N, int K, const int32_t* row_ptr, int B,
-                                int m_cap, float* partial, Epi epi, hipStream_t st) {
+                                int m_cap, float* partial, Epi epi, hipStream_t st,
+                                bool reduce = true) {
   GemmArgs g;
   g.X = X; g.W = W; g.W2 = W2; g.N = N; g.K = K;
   g.kchunk = kchunk_of(p, K);
   g.row_ptr = row_ptr; g.B = B; g.m_cap = m_cap;
   g.partial = (p.splits > 1) ? partial : nullptr;
-  const int ntile = SWIGLU ? cdiv(N, kBN / 2) : cdiv(N, kBN);
-  dim3 grid(ntile, cdiv(m_cap, p.bm), p.splits);
-  if (p.bm == 64)
-    hipLaunchKernelGGL((gemm_bf16_kernel<64, SWIGLU, Epi>), grid, dim3(256), 0, st, g, epi);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, SWIGLU, Epi>), grid, dim3(256), 0, st, g, epi);
+  const int cols = SWIGLU ? p.bn / 2 : p.bn;
+  dim3 grid(cdiv(N, cols), cdiv(m_cap, p.bm), p.splits);
+#define RS(bm, bn) ring_slots(bm, bn, 64, 4)
+  bool ok;
+  if constexpr (SWIGLU) {
+    ok = launch_if<128, 96, 64, 4, 1, RS(128, 96), true>(p, g, grid, epi, st) ||
+         launch_if<64, 96, 64, 2, 1, RS(64, 96), true>(p, g, grid, epi, st) ||
+         launch_if<128, 128, 64, 2, 2, 3, true>(p, g, grid, epi, st);
+  } else {
+    ok = launch_if<128, 48, 64, 4, 1, RS(128, 48), false>(p, g, grid, epi, st) ||
+         launch_if<128, 64, 64, 4, 1, RS(128, 64), false>(p, g, grid, epi, st) ||
+         launch_if<64, 48, 64, 2, 1, RS(64, 48), false>(p, g, grid, epi, st) ||
+         launch_if<64, 64, 64, 2, 1, RS(64, 64), false>(p, g, grid, epi, st) ||
+         launch_if<128, 128, 64, 2, 2, 3, false>(p, g, grid, epi, st);
+  }
+#undef RS
+  if (!ok) return hipErrorInvalidConfiguration;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  if constexpr (!SWIGLU) {
-    const size_t groups = (size_t)m_cap * (N / 4);
+  if (e != hipSuccess || p.splits == 1 || !reduce) return e;
+  const size_t groups = (size_t)m_cap * (N / 4);
+  if constexpr (SWIGLU)
+    hipLaunchKernelGGL((splitk_swiglu_kernel<Epi>), dim3((unsigned)((groups + 255) / 256)),
+                       dim3(256), 0, st, partial, p.splits, N, row_ptr, B, m_cap, epi);
+  else
     hipLaunchKernelGGL((splitk_reduce_kernel<Epi>), dim3((unsigned)((groups + 255) / 256)),
                        dim3(256), 0, st, partial, p.splits, N, row_ptr, B, m_cap, epi);
-  }
   return hipGetLastError();
 }
 
@@ -479,11 +605,49 @@ static hipError_t qkv_impl(const ProjShape& s, const T* h_in, const T* g_attn, c
   if (e != hipSuccess) return e;
   EpiQKV<T> epi{q_sel, kc, vc, sel_idx, Nq, Nkv, s.hd, s.S, s.Hkv};
   if constexpr (kBf16) {
-    GemmPlan p = plan_gemm(true, s.m_cap, N, s.d, true);
+    GemmPlan p = plan_gemm(true, s.m_cap, N, s.d, false);
     return run_gemm_bf16<false>(p, xn, w_qkv, nullptr, N, s.d, row_ptr, s.B, s.m_cap, partial,
                                 epi, st);
   } else {
     return run_gemm_f32<false>(xn, w_qkv, nullptr, N, s.d, row_ptr, s.B, s.m_cap, epi, st);
+  }
+}
+
+// h[j] = h_in[sel[j]] + sum_z partial[z][j] (fixed order); hn[j] = RMSNorm(h[j]) * g.
+// Finishes a K-split output projection and normalises its rows in one pass.
+template <typename T>
+__global__ __launch_bounds__(256) void resid_rmsnorm_kernel(const T* x, const int32_t* sel_idx,
+                                                            const float* partial, int splits,
+                                                            const T* g, float* h, T* hn, int d,
+                                                            float eps, const int32_t* row_ptr,
+                                                            int B, int m_cap) {
+  const int j = blockIdx.x;
+  if (j >= live_rows(row_ptr, B, m_cap)) return;
+  const T* xr = x + (size_t)sel_idx[j] * d;
+  __shared__ float red[4];
+  float ss = 0.f;
+  for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
+    float v[4];
+    Elem<T>::load4(xr + i, v);
+    for (int z = 0; z < splits; ++z) {
+      float p[4];
+      Elem<float>::load4(partial + ((size_t)z * m_cap + j) * d + i, p);
+      v[0] += p[0]; v[1] += p[1]; v[2] += p[2]; v[3] += p[3];
+    }
+    Elem<float>::store4(h + (size_t)j * d + i, v);
+    ss = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], ss))));
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+  // each thread re-reads only the h entries it wrote itself
+  for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
+    float v[4], gv[4];
+    Elem<float>::load4(h + (size_t)j * d + i, v);
+    Elem<T>::load4(g + i, gv);
+    const float o[4] = {v[0] * r * gv[0], v[1] * r * gv[1], v[2] * r * gv[2], v[3] * r * gv[3]};
+    Elem<T>::store4(hn + (size_t)j * d + i, o);
   }
 }
 
@@ -504,25 +668,33 @@ static hipError_t ffn_impl(const ProjShape& s, const T* h_in, const T* o_sel, co
   float* partial = reinterpret_cast<float*>(p);
   hipError_t e;
 
-  // h = h_in[sel] + o_sel W_o^T
+  // h = h_in[sel] + o_sel W_o^T ; hn = RMSNorm(h) * g_ffn
   EpiResidF32<T> e1{hbuf, h_in, sel_idx, s.d};
-  if constexpr (kBf16)
-    e = run_gemm_bf16<false>(plan_gemm(true, s.m_cap, s.d, Nq, true), o_sel, w_o, nullptr, s.d,
-                             Nq, row_ptr, s.B, s.m_cap, partial, e1, st);
-  else
+  if constexpr (kBf16) {
+    const GemmPlan po = plan_gemm(true, s.m_cap, s.d, Nq, false);
+    e = run_gemm_bf16<false>(po, o_sel, w_o, nullptr, s.d, Nq, row_ptr, s.B, s.m_cap, partial,
+                             e1, st, /*reduce=*/false);
+    if (e != hipSuccess) return e;
+    if (po.splits > 1)
+      hipLaunchKernelGGL((resid_rmsnorm_kernel<T>), dim3(s.m_cap), dim3(256), 0, st, h_in,
+                         sel_idx, partial, po.splits, g_ffn, hbuf, hn, s.d, s.eps, row_ptr, s.B,
+                         s.m_cap);
+    else
+      hipLaunchKernelGGL((rmsnorm_rows_kernel<float, T>), dim3(s.m_cap), dim3(256), 0, st, hbuf,
+                         nullptr, g_ffn, hn, s.d, s.eps, row_ptr, s.B, s.m_cap);
+  } else {
     e = run_gemm_f32<false>(o_sel, w_o, nullptr, s.d, Nq, row_ptr, s.B, s.m_cap, e1, st);
-  if (e != hipSuccess) return e;
-
-  // hn = RMSNorm(h) * g_ffn
-  hipLaunchKernelGGL((rmsnorm_rows_kernel<float, T>), dim3(s.m_cap), dim3(256), 0, st, hbuf,
-                     nullptr, g_ffn, hn, s.d, s.eps, row_ptr, s.B, s.m_cap);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((rmsnorm_rows_kernel<float, T>), dim3(s.m_cap), dim3(256), 0, st, hbuf,
+                       nullptr, g_ffn, hn, s.d, s.eps, row_ptr, s.B, s.m_cap);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // z = silu(hn W_gate^T) * (hn W_up^T)
   EpiSwiGLU<T> e2{z, s.F};
   if constexpr (kBf16)
-    e = run_gemm_bf16<true>(plan_gemm(true, s.m_cap, 2 * s.F, s.d, false), hn, w_gate, w_up, s.F,
-                            s.d, row_ptr, s.B, s.m_cap, nullptr, e2, st);
+    e = run_gemm_bf16<true>(plan_gemm(true, s.m_cap, s.F, s.d, true), hn, w_gate, w_up, s.F, s.d,
+                            row_ptr, s.B, s.m_cap, partial, e2, st);
   else
     e = run_gemm_f32<true>(hn, w_gate, w_up, s.F, s.d, row_ptr, s.B, s.m_cap, e2, st);
   if (e != hipSuccess) return e;
@@ -530,7 +702,7 @@ static hipError_t ffn_impl(const ProjShape& s, const T* h_in, const T* o_sel, co
   // h_out[sel] = h + z W_down^T
   EpiResidScatter<T> e3{h_out, hbuf, sel_idx, s.d};
   if constexpr (kBf16)
-    e = run_gemm_bf16<false>(plan_gemm(true, s.m_cap, s.d, s.F, true), z, w_down, nullptr, s.d,
+    e = run_gemm_bf16<false>(plan_gemm(true, s.m_cap, s.d, s.F, false), z, w_down, nullptr, s.d,
                              s.F, row_ptr, s.B, s.m_cap, partial, e3, st);
   else
     e = run_gemm_f32<false>(z, w_down, nullptr, s.d, s.F, row_ptr, s.B, s.m_cap, e3, st);

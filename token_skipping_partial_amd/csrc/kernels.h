@@ -40,10 +40,15 @@ struct ProjShape {
 
 // launch plan of one GEMM: tile height, number of K splits
 struct GemmPlan {
-  int bm;      // 64 or 128 rows per tile (bf16); fp32 path uses its own tiles
+  int bm;      // rows of X per tile (bf16: 64 or 128); the fp32 path uses 64 x 64 tiles
+  int bn;      // weight rows per tile (SwiGLU: gate + up rows)
+  int bk;      // K columns per LDS ring slot (64 or 128)
+  int wm, wn;  // wave grid
+  int st;      // ring slots
   int splits;  // K partitions reduced in a second pass (1 = fused epilogue)
 };
-GemmPlan plan_gemm(bool bf16, int m_cap, int N, int K, bool splittable);
+// N = output columns (SwiGLU: F, the tile then holds gate and up rows of the same columns)
+GemmPlan plan_gemm(bool bf16, int m_cap, int N, int K, bool swiglu);
 size_t gemm_partials_bytes(const GemmPlan& p, int m_cap, int N);
 
 size_t qkv_workspace_bytes(bool bf16, const ProjShape& s);
