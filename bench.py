@@ -43,7 +43,23 @@ def parse():
     p.add_argument("--sets", type=int, default=16, help="rotated input/weight sets")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget of the CPU oracle sample (0 = skip)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run 5 plain device copies of 1 GiB (reference for rocprofv3 "
+                        "FETCH_SIZE / WRITE_SIZE scaling) and exit")
     return p.parse_args()
+
+
+def calibrate_copy():
+    """Five device-to-device copies of exactly 1 GiB (read 1 GiB + write 1 GiB per launch)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "launches": 5}), flush=True)
 
 
 def kernel_traffic(kernel: str, source: str):
@@ -70,6 +86,10 @@ def main():
         print("bench.py measures one GPU only: this build runs the token-skipping step on a single "
               "MI355X (no collectives). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import token_skipping_partial_amd as tsp  # raises if libdllm.so is not built
     from synth import workloads as W

@@ -263,10 +263,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g, Epi
   const int n0 = blockIdx.x * (SWIGLU ? BN / 2 : BN);
   const int kb = blockIdx.z * g.kchunk;
   const int nk = (min(g.K, kb + g.kchunk) - kb) / BK;  // >= 1 by the plan
-  // Each workgroup starts its K walk at a different slot: workgroups running side by side then
-  // read different column offsets of their weight rows instead of the same offset of rows a
-  // power-of-two stride apart. The order is a fixed function of the tile (deterministic).
-  const int rot = (int)((blockIdx.x * 37u + blockIdx.y * 11u) % (unsigned)nk);
+  // All workgroups walk K in the same order: tiles that share an X slice then read it at about
+  // the same time, so it is fetched into each L2 once instead of being evicted by the weight
+  // stream between readers.
+  const int rot = 0;
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / WN, wn = wave % WN;
