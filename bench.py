@@ -39,7 +39,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="llada_layer", choices=["llada_layer"])
+    p.add_argument("--workload", default="llada_layer", choices=["llada_layer", "llada_step"],
+                   help="llada_layer: one LLaDA-8B-shaped layer, B=1 (default); llada_step: the "
+                        "full 32-layer early-skip step, B=8, S=1024, top-205 per sequence")
     p.add_argument("--sets", type=int, default=16, help="rotated input/weight sets")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget of the CPU oracle sample (0 = skip)")
@@ -89,6 +91,10 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+
+    if args.workload == "llada_step":
+        run_llada_step(args)
         return
 
     import token_skipping_partial_amd as tsp  # raises if libdllm.so is not built
@@ -226,6 +232,60 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in kernels.items()},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_llada_step(args):
+    """32 LLaDA-8B layers, B=8, S=1024: layers 0-3 on every token, saliency at layer 4 (alpha 0.5,
+    fresh previous-step logits), top-205 per sequence, layers 4-31 on the selected rows against the
+    cached K/V. Hidden input X^t = X^(t-1) + per-step perturbation; caches carried across steps."""
+    import synth
+    import token_skipping_partial_amd as tsp
+    from synth import workloads as W
+    from token_skipping_partial_amd.step import EarlySkipModel, LayerWeights, SelectConfig
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dims, L, skip, k_sel = W.LLADA_STEP, 32, W.STEP_SKIP, W.STEP_TOPK
+    shape = tsp.Shape(B=dims.B, S=dims.S, d=dims.d, H=dims.H, Hkv=dims.Hkv, hd=dims.hd,
+                      F=dims.F, dtype="bf16", V=dims.V)
+    print(f"[bench] llada_step: {L} layers of {shape}", file=sys.stderr, flush=True)
+    layers = [LayerWeights.from_dict(synth.layer_weights(dims.d, dims.H, dims.Hkv, dims.hd, dims.F,
+                                                         seed=7000 + l, device="cuda"))
+              for l in range(L)]
+    model = EarlySkipModel(shape, layers, skip, SelectConfig(mode=tsp.SEL_TOPK, k=k_sel, alpha=0.5),
+                           m_cap=dims.B * k_sel)
+    nsteps = args.warmup + args.steps
+    xs = [synth.normal((dims.B, dims.S, dims.d), 1.0, 7500, torch.bfloat16, "cuda")]
+    for t in range(1, nsteps + 1):
+        large = synth.large_positions(dims.B, dims.S, W.LLADA_LARGE, seed=7600 + t, device="cuda")
+        xs.append(synth.perturb(xs[-1], large, seed=7700 + t))
+    logits = [synth.logits(dims.B, dims.S, dims.V, seed=7800 + i, device="cuda") for i in range(4)]
+    model.fill(xs[0])
+    for t in range(args.warmup):
+        model.step(xs[1 + t], logits[t % 4])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for t in range(args.steps):
+        i = args.warmup + t
+        model.step(xs[1 + i], logits[i % 4])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    M = int(model.step1.row_ptr[-1].item())
+    units = skip * dims.B * dims.S + (L - skip) * M
+    out = {
+        "metric": METRIC, "value": round(units / (ms * 1e-3), 1),
+        "unit": "selected-token layer-steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: X0 N(0,1), per step 154 tokens per sequence + N(0,0.5^2), rest + "
+                "N(0,(1e-3)^2); logits N(0,3^2); random-init weights N(0,0.02^2)",
+        "config": {"workload": "llada_step: 32 LLaDA-8B-shaped layers, B=8, S=1024, early skip at "
+                               "layer 4, alpha=0.5, top-205 per sequence",
+                   "units_per_step": units, "selected_per_step": M},
     }
     print(json.dumps(out), flush=True)
 

@@ -5,10 +5,12 @@
 // cached position (no mask), including masked tokens and itself, with the K/V entries that the
 // projection call of this step has just overwritten.
 //
-// Work decomposition: one workgroup = 64 query rows of one (sequence b, kv head hk) against a
-// key range. A "query row" is a (selected token, query head of hk's group) pair, so grouped
-// heads share every K/V tile that is loaded (GQA packing). Per 64-key tile:
-//   * K rows -> LDS; V rows -> LDS transposed ([hd][key]);
+// Work decomposition: one workgroup = 128 query rows (4 waves x two 16-row blocks) of one
+// (sequence b, kv head hk) against a key range. A "query row" is a (selected token, query head of
+// hk's group) pair, so grouped heads share every K/V tile that is loaded (GQA packing), and each
+// K/V fragment read from LDS feeds the MFMAs of both query blocks of a wave. Per 64-key tile:
+//   * K rows -> LDS; V rows -> LDS transposed ([hd][key]); the next tile's K/V loads are issued
+//     into registers before this tile is multiplied, so their latency hides behind the MFMAs;
 //   * S^T = K Q^T on the bf16 matrix cores (16x16x32): the lane's accumulator column is ONE
 //     query, so the online-softmax max/sum over keys is a 2-step cross-lane shuffle;
 //   * within each 32-key group the keys feeding the two 16-row S^T blocks are interleaved
@@ -23,8 +25,9 @@
 
 namespace dllm {
 
-constexpr int kTQ = 64;  // query rows per workgroup (4 waves x 16)
-constexpr int kTK = 64;  // keys per tile
+constexpr int kQB = 2;             // 16-row query blocks per wave
+constexpr int kTQ = 64 * kQB;      // query rows per workgroup (4 waves x 2 blocks x 16)
+constexpr int kTK = 64;            // keys per tile
 constexpr int kVtPitch = kTK + 8;
 
 struct AttnArgs {
@@ -39,6 +42,9 @@ struct AttnArgs {
   float scale_log2;  // scale * log2(e): scores are kept in base-2 units
 };
 
+// grid.x enumerates (sequence, kv head, key split) and grid.y the query tiles, so the tiles that
+// share one K/V panel have ids grid.x apart: with grid.x a multiple of 8 they run on the same XCD
+// and read the panel through one L2.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KB = HD / 32;         // 32-wide k-steps of q.k over hd
@@ -51,12 +57,14 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 
   const int G = a.H / a.Hkv;
   const int Nq = a.H * HD;
-  const int b = blockIdx.z;
-  const int hk = blockIdx.y / a.nsplit, split = blockIdx.y - hk * a.nsplit;
+  const int per_b = a.Hkv * a.nsplit;
+  const int b = blockIdx.x / per_b;
+  const int hk = (blockIdx.x - b * per_b) / a.nsplit;
+  const int split = blockIdx.x - b * per_b - hk * a.nsplit;
   const int M = min(a.row_ptr[a.B], a.m_cap);
   const int r0 = min(a.row_ptr[b], M), r1 = min(a.row_ptr[b + 1], M);
   const int nrows = (r1 - r0) * G;
-  const int tile0 = blockIdx.x * kTQ;
+  const int tile0 = blockIdx.y * kTQ;
   if (tile0 >= nrows) return;
   const int t0 = split * a.kps;
   const int t1 = min(a.S, t0 + a.kps);
@@ -64,27 +72,31 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
 
-  // ---- this lane's query row = column lr of the wave's S^T block
-  const int qr = tile0 + wave * 16 + lr;
-  const bool qvalid = qr < nrows;
-  int j = 0, h = 0;
-  if (qvalid) {
-    j = r0 + qr / G;
-    h = hk * G + qr % G;
-  }
-  bf16x8 qf[KB];
+  // ---- this lane's query rows: column lr of each of the wave's S^T blocks
+  bool qvalid[kQB];
+  int qj[kQB], qh[kQB];
+  bf16x8 qf[kQB][KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    if (qvalid)
-      qf[kb] = *reinterpret_cast<const bf16x8*>(a.q + (size_t)j * Nq + h * HD + kb * 32 + lg * 8);
-    else
-      qf[kb] = bf16x8{};
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int qr = tile0 + wave * (16 * kQB) + qb * 16 + lr;
+    qvalid[qb] = qr < nrows;
+    qj[qb] = qvalid[qb] ? r0 + qr / G : 0;
+    qh[qb] = qvalid[qb] ? hk * G + qr % G : 0;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      qf[qb][kb] = qvalid[qb] ? *reinterpret_cast<const bf16x8*>(a.q + (size_t)qj[qb] * Nq +
+                                                                 qh[qb] * HD + kb * 32 + lg * 8)
+                              : bf16x8{};
   }
 
-  f32x4 oacc[HB];
+  f32x4 oacc[kQB][HB];
 #pragma unroll
-  for (int i = 0; i < HB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+    for (int i = 0; i < HB; ++i) oacc[qb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[kQB], l_run[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; }
 
   const size_t head_off = ((size_t)b * a.Hkv + hk) * (size_t)a.S * HD;
   const uint16_t* kbase = a.kc + head_off;
@@ -93,20 +105,23 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   // K load: chunks tid + 256 i -> (row, 8-col); V load: KPT consecutive keys x 8 hd columns
   const int vkg = tid / KCH, vcol = (tid % KCH) * 8;
   uint4 kreg[KPT], vreg[KPT];
-
-  for (int tk = t0; tk < t1; tk += kTK) {
+  auto load_tile = [&](int tk) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + 256 * i;
-      const int row = c / KCH, col = (c % KCH) * 8;
-      const int key = tk + row;
-      kreg[i] = (key < t1) ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * HD + col)
+      const int key = tk + c / KCH;
+      kreg[i] = (key < t1) ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * HD +
+                                                              (c % KCH) * 8)
                            : make_uint4(0, 0, 0, 0);
       const int vkey = tk + vkg * KPT + i;
       vreg[i] = (vkey < t1) ? *reinterpret_cast<const uint4*>(vbase + (size_t)vkey * HD + vcol)
                             : make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();  // the previous tile's LDS reads are done
+  };
+
+  load_tile(t0);
+  for (int tk = t0; tk < t1; tk += kTK) {
+    __syncthreads();  // every wave is done reading the previous tile
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + 256 * i;
@@ -132,92 +147,102 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
+    // the next tile's loads fly while this one is multiplied
+    if (tk + kTK < t1) load_tile(tk + kTK);
 
     // ---- S^T blocks: blk = 2 ks + half, row m <-> key 32 ks + 8 (m/4) + 4 half + m%4
-    f32x4 sacc[4];
+    f32x4 sacc[kQB][4];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       const int ks = blk >> 1, half = blk & 1;
       const int kr = 32 * ks + 8 * (lr >> 2) + 4 * half + (lr & 3);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) sacc[qb][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + kr * KPitch + kb * 32 + lg * 8);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kb], acc, 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          sacc[qb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][kb], sacc[qb][blk],
+                                                                   0, 0, 0);
       }
-      sacc[blk] = acc;
     }
-    // sacc[blk][i] = score of query lr with key tk + 32 ks + 8 lg + 4 half + i
-    float sv[4][4];
-    float mx = -INFINITY;
+    // sacc[qb][blk][i] = score of query (qb, lr) with key tk + 32 ks + 8 lg + 4 half + i
+    bf16x8 pf[kQB][2];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk)
+    for (int qb = 0; qb < kQB; ++qb) {
+      float sv[4][4];
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = tk + 32 * (blk >> 1) + 8 * lg + 4 * (blk & 1) + i;
-        sv[blk][i] = (key < t1) ? sacc[blk][i] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[blk][i]);
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = tk + 32 * (blk >> 1) + 8 * lg + 4 * (blk & 1) + i;
+          sv[blk][i] = (key < t1) ? sacc[qb][blk][i] * a.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sv[blk][i]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[qb], mx);
+      const float alpha = fast_exp2(m_run[qb] - m_new);  // 0 on the first tile
+      float psum = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(sv[blk][i] - m_new);
+          psum += p;
+          pf[qb][blk >> 1][4 * (blk & 1) + i] = (__bf16)p;
+        }
+      l_run[qb] = l_run[qb] * alpha + psum;
+      m_run[qb] = m_new;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        oacc[qb][hb][0] *= alpha; oacc[qb][hb][1] *= alpha;
+        oacc[qb][hb][2] *= alpha; oacc[qb][hb][3] *= alpha;
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
-    float psum = 0.f;
-    float p[4][4];
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[blk][i] = fast_exp2(sv[blk][i] - m_new);
-        psum += p[blk][i];
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      oacc[hb][0] *= alpha; oacc[hb][1] *= alpha; oacc[hb][2] *= alpha; oacc[hb][3] *= alpha;
     }
     // ---- O^T += V^T P^T; the k-slot s of lane group lg is key 32 ks + 8 lg + s
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pf[i] = (__bf16)p[2 * ks][i];
-        pf[4 + i] = (__bf16)p[2 * ks + 1][i];
-      }
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sVt + (hb * 16 + lr) * kVtPitch +
                                                            32 * ks + 8 * lg);
-        oacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[hb], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          oacc[qb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb][ks], oacc[qb][hb],
+                                                                  0, 0, 0);
       }
-    }
   }
 
-  // oacc[hb][i] = unnormalised o[query lr][hd = 16 hb + 4 lg + i]; this lane's sum covers a
-  // quarter of the keys
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (!qvalid) return;
-  if (a.nsplit == 1) {
-    const float inv = 1.0f / l_tot;
+  // oacc[qb][hb][i] = unnormalised o[query (qb, lr)][hd = 16 hb + 4 lg + i]; this lane's sum
+  // covers a quarter of the keys
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const float v[4] = {oacc[hb][0] * inv, oacc[hb][1] * inv, oacc[hb][2] * inv,
-                          oacc[hb][3] * inv};
-      Elem<uint16_t>::store4(a.o + (size_t)j * Nq + h * HD + hb * 16 + 4 * lg, v);
-    }
-  } else {
-    const size_t base = ((size_t)split * a.m_cap + j) * a.H + h;
+  for (int qb = 0; qb < kQB; ++qb) {
+    float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (!qvalid[qb]) continue;
+    const int j = qj[qb], h = qh[qb];
+    if (a.nsplit == 1) {
+      const float inv = 1.0f / l_tot;
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const float v[4] = {oacc[hb][0], oacc[hb][1], oacc[hb][2], oacc[hb][3]};
-      Elem<float>::store4(a.part_o + base * HD + hb * 16 + 4 * lg, v);
-    }
-    if (lg == 0) {
-      a.part_ml[base * 2] = m_run;
-      a.part_ml[base * 2 + 1] = l_tot;
+      for (int hb = 0; hb < HB; ++hb) {
+        const float v[4] = {oacc[qb][hb][0] * inv, oacc[qb][hb][1] * inv, oacc[qb][hb][2] * inv,
+                            oacc[qb][hb][3] * inv};
+        Elem<uint16_t>::store4(a.o + (size_t)j * Nq + h * HD + hb * 16 + 4 * lg, v);
+      }
+    } else {
+      const size_t base = ((size_t)split * a.m_cap + j) * a.H + h;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const float v[4] = {oacc[qb][hb][0], oacc[qb][hb][1], oacc[qb][hb][2], oacc[qb][hb][3]};
+        Elem<float>::store4(a.part_o + base * HD + hb * 16 + 4 * lg, v);
+      }
+      if (lg == 0) {
+        a.part_ml[base * 2] = m_run[qb];
+        a.part_ml[base * 2 + 1] = l_tot;
+      }
     }
   }
 }
@@ -305,7 +330,7 @@ static void split_keys(bool bf16, const ProjShape& s, int& nsplit, int& kps) {
     const int G = s.H / s.Hkv;
     const long est = (long)(cdiv((long)s.m_cap * G, kTQ) > 0 ? cdiv((long)s.m_cap * G, kTQ) : 1) *
                      s.Hkv;
-    while (est * nsplit < 512 && s.S / (nsplit * 2) >= 256) nsplit *= 2;
+    while (est * nsplit < 512 && s.S / (nsplit * 2) >= 128) nsplit *= 2;
   }
   kps = cdiv(cdiv(s.S, nsplit), kTK) * kTK;
   nsplit = cdiv(s.S, kps);  // every split owns at least one key
@@ -353,7 +378,7 @@ hipError_t launch_attn(bool bf16, const ProjShape& s, float scale, const void* q
   }
   const int G = s.H / s.Hkv;
   const int rows_max = (s.m_cap < s.S ? s.m_cap : s.S) * G;
-  dim3 grid(cdiv(rows_max, kTQ), s.Hkv * a.nsplit, s.B);
+  dim3 grid(s.B * s.Hkv * a.nsplit, cdiv(rows_max, kTQ));
   if (s.hd == 64)
     hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, st, a);
   else
