@@ -191,7 +191,7 @@ def test_qkv_scatter(lib, case, cap):
 
 # ----------------------------------------------------------------------------- (4) attention
 ATTN_CASES = {
-    # dtype, B, S, H, Hkv, hd, counts, q scale
+    # dtype, B, S, H, Hkv, hd, counts, q scale[, softmax scale (default 1/sqrt(hd)), key ramp]
     "f32_tiny": (F32, 1, 64, 4, 4, 64, [16], 1.0),
     "f32_gqa": (F32, 2, 130, 4, 2, 128, [5, 9], 1.0),
     "llada_b1_m128": (BF16, 1, 1024, 32, 32, 128, [128], 1.0),
@@ -201,22 +201,34 @@ ATTN_CASES = {
     "seq_len_1": (BF16, 3, 1, 4, 4, 128, [1, 1, 0], 1.0),
     "peaked": (BF16, 1, 777, 4, 1, 128, [65], 6.0),
     "long_4096": (BF16, 1, 4096, 8, 8, 128, [96], 1.0),
+    # scores that rise by about one (base 2) per 64-key tile: the running maximum creeps up by
+    # less than the rescaling slack at each tile, so unnormalised probabilities far above 1
+    # accumulate between rescalings
+    "rising_keys": (BF16, 2, 1000, 8, 2, 128, [40, 130], 1.0, None, True),
+    "negative_scale": (BF16, 2, 200, 8, 4, 128, [30, 77], 1.0, -0.2),
+    "zero_scale": (BF16, 1, 150, 4, 4, 64, [20], 1.0, 0.0),
 }
 
 
 @pytest.mark.parametrize("case", list(ATTN_CASES))
 def test_partial_attn(lib, case):
-    dtype, B, S, H, Hkv, hd, counts, qs = ATTN_CASES[case]
+    dtype, B, S, H, Hkv, hd, counts, qs, *extra = ATTN_CASES[case]
+    sc = extra[0] if extra and extra[0] is not None else 1.0 / math.sqrt(hd)
+    ramp = len(extra) > 1 and extra[1]
     print(f"attn case={case}", flush=True)
     sel, rp = random_selection(B, S, counts, 500)
     M = int(rp[-1])
-    q = (synth.normal((max(1, M), H * hd), qs, 501, F32)).to(dtype)
-    kc = synth.normal((B, Hkv, S, hd), 1.0, 502, dtype)
+    q = synth.normal((max(1, M), H * hd), qs, 501, F32)
+    kc = synth.normal((B, Hkv, S, hd), 1.0, 502, F32)
+    if ramp:  # every entry of q shifted by +1 and of key t by t / S: q.k grows by ~hd t / S
+        q = q + 1.0
+        kc = kc + torch.linspace(0.0, 1.0, S)[None, None, :, None]
+    q, kc = q.to(dtype), kc.to(dtype)
     vc = synth.normal((B, Hkv, S, hd), 1.0, 503, dtype)
     shape = shape_of(lib, dtype, B, S, 64, H, Hkv, hd, 64)
     o = torch.full((max(1, M), H * hd), -3.0, dtype=dtype, device="cuda")
     ws = lib.workspace(lib.OP_ATTN, shape, M)
-    scale = 1.0 / math.sqrt(hd)
+    scale = sc
     lib.dllm_partial_attn(shape, scale, to_dev(q), to_dev(kc), to_dev(vc), to_dev(sel), to_dev(rp),
                           M, o, ws)
     torch.cuda.synchronize()
