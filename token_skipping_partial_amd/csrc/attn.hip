@@ -5,21 +5,22 @@
 // cached position (no mask), including masked tokens and itself, with the K/V entries that the
 // projection call of this step has just overwritten.
 //
-// Work decomposition: one workgroup = 128 query rows (4 waves x two 16-row blocks) of one
-// (sequence b, kv head hk) against a key range. A "query row" is a (selected token, query head of
-// hk's group) pair, so grouped heads share every K/V tile that is loaded (GQA packing), and each
-// K/V fragment read from LDS feeds the MFMAs of both query blocks of a wave. Per 64-key tile:
-//   * K rows -> LDS; V rows -> LDS transposed ([hd][key]); the next tile's K/V loads are issued
-//     into registers before this tile is multiplied, so their latency hides behind the MFMAs;
-//   * S^T = K Q^T on the bf16 matrix cores (16x16x32): the lane's accumulator column is ONE
-//     query, so the online-softmax max/sum over keys is a 2-step cross-lane shuffle;
-//   * within each 32-key group the keys feeding the two 16-row S^T blocks are interleaved
-//     (block 0: keys 8g+0..3, block 1: keys 8g+4..7 for lane group g) so that the exponentiated
-//     scores already sit in registers in the B-operand layout of the next product;
-//   * O^T += V^T P^T on the matrix cores, fp32 accumulation, rescaled by the running max.
-// When the selected rows alone cannot fill the 256 compute units (batch 1, M = 128), the key
-// range is split and the fp32 partials (o, max, sum) are merged in a fixed order by a second
-// pass, so results stay deterministic.
+// Work decomposition: one workgroup = NW waves x 32 query rows of one (sequence b, kv head hk)
+// against a key range. A "query row" is a (selected token, query head of hk's group) pair, so
+// grouped heads share every K/V tile that is loaded (GQA packing). Per 64-key tile:
+//   * K and V rows go straight from global memory into an LDS ring (direct-to-LDS loads issued
+//     several tiles ahead), in their natural [key][hd] layout with a 16-byte-chunk swizzle;
+//   * S^T = K Q^T on the bf16 matrix cores in 32x32x16 blocks (two per tile): the lane's
+//     accumulator column is one query, so the lane owns 32 of its 64 scores;
+//   * the 32 keys of an S^T block are permuted so that the exponentiated scores already sit in
+//     the B-operand layout of the next product (4 chunks of 16 keys, 8 per lane);
+//   * O^T += V^T P^T in 32x32x16 blocks; the V^T fragments come from the natural-layout V rows
+//     through the transposing LDS read, fp32 accumulation.
+// The exponentials use a lazily moved reference point: it moves (and the accumulators are
+// rescaled) only when a tile's maximum exceeds it by more than 2^kLazy, so the common tile needs
+// no cross-lane traffic. When the selected rows alone cannot fill the 256 compute units, the key
+// range is split and the fp32 partials (o, reference, sum) are merged in a fixed order by a
+// second pass, so results stay deterministic.
 #include <type_traits>
 
 #include "common.h"
@@ -27,14 +28,8 @@
 
 namespace dllm {
 
-constexpr int kQB = 2;             // 16-row query blocks per wave
-constexpr int kTQ = 64 * kQB;      // query rows per workgroup (4 waves x 2 blocks x 16)
-constexpr int kTK = 64;            // keys per tile
-constexpr float kLazy = 8.f;       // running-max slack before the accumulators are rescaled
-#ifndef DLLM_ATTN_ST
-#define DLLM_ATTN_ST 2
-#endif
-constexpr int kAttnST = DLLM_ATTN_ST;  // LDS ring slots (tiles in flight + the one being used)
+constexpr int kTK = 64;         // keys per tile
+constexpr float kLazy = 8.f;    // reference-point slack (base-2 units) before rescaling
 
 struct AttnArgs {
   const uint16_t* q;
@@ -50,135 +45,160 @@ struct AttnArgs {
 
 typedef __attribute__((address_space(3))) void lds_void_a;
 typedef short __attribute__((ext_vector_type(4))) s16x4;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int N>
 __device__ __forceinline__ void attn_wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-// 16-byte chunk swizzle of a K or V row of 8 or 16 chunks, a function of row bits 0, 1, 3, 4. A K
-// fragment read touches, per 16-lane group, the 16 rows in which those bits vary: they land on 16
-// distinct chunk positions (256-byte rows) or on distinct (row parity, chunk) positions (128-byte
-// rows). A transposing V read touches, per 32 lanes, 8 rows in which bits 0, 1, 3 vary, 32 bytes
-// (one aligned chunk pair) each: the pair index depends on exactly those bits, so the 8 rows cover
-// all banks once.
+
+// 16-byte chunk swizzles of the K and V rows (CPR chunks per row).
+// K: a fragment read touches, per 16-lane group, 16 key rows whose bits 0-3 vary; they land on
+// 16 distinct chunk positions (256-byte rows) or distinct (row parity, chunk) positions (128-byte
+// rows). V: a transposing read touches, per 32 lanes, 4 rows whose bits 0-1 vary, 64 bytes each;
+// those bits select distinct 64-byte groups of the 256 bank bytes. The V swizzle ignores row
+// bits 2, 4 and 5, so the reads 4 and 16 rows further are plain byte offsets.
 template <int CPR>
-__device__ __forceinline__ int aswz(int r) {
-  if constexpr (CPR == 8) return ((r >> 4) & 1) | (r & 2) | ((r >> 1) & 4);
-  else return ((r >> 4) & 1) | ((r & 3) << 1) | (r & 8);
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (CPR == 8) return (r >> 1) & 7;
+  else return r & 15;
+}
+template <int CPR>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (CPR == 8) return (r & 2) << 1;
+  else return (r & 3) << 2;
 }
 
-// V^T fragments of one 32-key group KS for every 16-wide hd block, read from V rows in their
-// natural [key][hd] layout by the transposing LDS read (lane i of a 16-lane group receives, for each
-// of the 4 keys addressed by lanes 4k .. 4k+3, the value at hd column i of the block). addr[hb] is
-// the LDS byte address of the lane's first row (key 8 lg + q/4) for block hb; the second read of
-// each block covers the keys 4 rows further, and group KS sits 32 rows further. The reads wait for
-// their own completion inside the asm statement, so no result register is live while a read is
+// V^T fragments of one 16-key chunk CC for every 32-wide hd block, read from V rows in their
+// natural [key][hd] layout by the transposing LDS read (per 16-lane group, lane i receives for each
+// of the 4 rows addressed by lanes 4k .. 4k+3 the value at column i of the 16 columns they cover).
+// addr[hb] is the LDS byte address of the lane's row (8 (lane/32) + q/4 of chunk 0); the second
+// read of each block covers the rows 4 further, chunk CC sits 16 CC rows further. The reads wait
+// for their own completion inside the asm statement, so no result register is live while a read is
 // still in flight. Written as asm because the compiler otherwise drains every outstanding
 // direct-to-LDS K/V load before each transposing read.
 template <int HD>
 struct VtFrag;
 template <>
 struct VtFrag<128> {
-  template <int KS>
-  static __device__ __forceinline__ void read(const uint32_t (&addr)[8], s16x4 (&lo)[8],
-                                              s16x4 (&hi)[8]) {
-    if constexpr (KS == 0)
-      asm volatile(
-        "ds_read_b64_tr_b16 %0, %16 offset:0\n"
-        "ds_read_b64_tr_b16 %1, %16 offset:1024\n"
-        "ds_read_b64_tr_b16 %2, %17 offset:0\n"
-        "ds_read_b64_tr_b16 %3, %17 offset:1024\n"
-        "ds_read_b64_tr_b16 %4, %18 offset:0\n"
-        "ds_read_b64_tr_b16 %5, %18 offset:1024\n"
-        "ds_read_b64_tr_b16 %6, %19 offset:0\n"
-        "ds_read_b64_tr_b16 %7, %19 offset:1024\n"
-        "ds_read_b64_tr_b16 %8, %20 offset:0\n"
-        "ds_read_b64_tr_b16 %9, %20 offset:1024\n"
-        "ds_read_b64_tr_b16 %10, %21 offset:0\n"
-        "ds_read_b64_tr_b16 %11, %21 offset:1024\n"
-        "ds_read_b64_tr_b16 %12, %22 offset:0\n"
-        "ds_read_b64_tr_b16 %13, %22 offset:1024\n"
-        "ds_read_b64_tr_b16 %14, %23 offset:0\n"
-        "ds_read_b64_tr_b16 %15, %23 offset:1024\n"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]), "=&v"(lo[6]), "=&v"(hi[6]), "=&v"(lo[7]), "=&v"(hi[7])
-        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]), "v"(addr[7]));
-    else
-      asm volatile(
-        "ds_read_b64_tr_b16 %0, %16 offset:8192\n"
-        "ds_read_b64_tr_b16 %1, %16 offset:9216\n"
-        "ds_read_b64_tr_b16 %2, %17 offset:8192\n"
-        "ds_read_b64_tr_b16 %3, %17 offset:9216\n"
-        "ds_read_b64_tr_b16 %4, %18 offset:8192\n"
-        "ds_read_b64_tr_b16 %5, %18 offset:9216\n"
-        "ds_read_b64_tr_b16 %6, %19 offset:8192\n"
-        "ds_read_b64_tr_b16 %7, %19 offset:9216\n"
-        "ds_read_b64_tr_b16 %8, %20 offset:8192\n"
-        "ds_read_b64_tr_b16 %9, %20 offset:9216\n"
-        "ds_read_b64_tr_b16 %10, %21 offset:8192\n"
-        "ds_read_b64_tr_b16 %11, %21 offset:9216\n"
-        "ds_read_b64_tr_b16 %12, %22 offset:8192\n"
-        "ds_read_b64_tr_b16 %13, %22 offset:9216\n"
-        "ds_read_b64_tr_b16 %14, %23 offset:8192\n"
-        "ds_read_b64_tr_b16 %15, %23 offset:9216\n"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]), "=&v"(lo[6]), "=&v"(hi[6]), "=&v"(lo[7]), "=&v"(hi[7])
-        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]), "v"(addr[7]));
-  }
-};
-template <>
-struct VtFrag<64> {
-  template <int KS>
+  template <int CC>
   static __device__ __forceinline__ void read(const uint32_t (&addr)[4], s16x4 (&lo)[4],
                                               s16x4 (&hi)[4]) {
-    if constexpr (KS == 0)
+    if constexpr (CC == 0)
       asm volatile(
         "ds_read_b64_tr_b16 %0, %8 offset:0\n"
-        "ds_read_b64_tr_b16 %1, %8 offset:512\n"
+        "ds_read_b64_tr_b16 %1, %8 offset:1024\n"
         "ds_read_b64_tr_b16 %2, %9 offset:0\n"
-        "ds_read_b64_tr_b16 %3, %9 offset:512\n"
+        "ds_read_b64_tr_b16 %3, %9 offset:1024\n"
         "ds_read_b64_tr_b16 %4, %10 offset:0\n"
-        "ds_read_b64_tr_b16 %5, %10 offset:512\n"
+        "ds_read_b64_tr_b16 %5, %10 offset:1024\n"
         "ds_read_b64_tr_b16 %6, %11 offset:0\n"
-        "ds_read_b64_tr_b16 %7, %11 offset:512\n"
+        "ds_read_b64_tr_b16 %7, %11 offset:1024\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]));
+    else if constexpr (CC == 1)
+      asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:4096\n"
+        "ds_read_b64_tr_b16 %1, %8 offset:5120\n"
+        "ds_read_b64_tr_b16 %2, %9 offset:4096\n"
+        "ds_read_b64_tr_b16 %3, %9 offset:5120\n"
+        "ds_read_b64_tr_b16 %4, %10 offset:4096\n"
+        "ds_read_b64_tr_b16 %5, %10 offset:5120\n"
+        "ds_read_b64_tr_b16 %6, %11 offset:4096\n"
+        "ds_read_b64_tr_b16 %7, %11 offset:5120\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]));
+    else if constexpr (CC == 2)
+      asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:8192\n"
+        "ds_read_b64_tr_b16 %1, %8 offset:9216\n"
+        "ds_read_b64_tr_b16 %2, %9 offset:8192\n"
+        "ds_read_b64_tr_b16 %3, %9 offset:9216\n"
+        "ds_read_b64_tr_b16 %4, %10 offset:8192\n"
+        "ds_read_b64_tr_b16 %5, %10 offset:9216\n"
+        "ds_read_b64_tr_b16 %6, %11 offset:8192\n"
+        "ds_read_b64_tr_b16 %7, %11 offset:9216\n"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3])
         : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]));
     else
       asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:4096\n"
-        "ds_read_b64_tr_b16 %1, %8 offset:4608\n"
-        "ds_read_b64_tr_b16 %2, %9 offset:4096\n"
-        "ds_read_b64_tr_b16 %3, %9 offset:4608\n"
-        "ds_read_b64_tr_b16 %4, %10 offset:4096\n"
-        "ds_read_b64_tr_b16 %5, %10 offset:4608\n"
-        "ds_read_b64_tr_b16 %6, %11 offset:4096\n"
-        "ds_read_b64_tr_b16 %7, %11 offset:4608\n"
+        "ds_read_b64_tr_b16 %0, %8 offset:12288\n"
+        "ds_read_b64_tr_b16 %1, %8 offset:13312\n"
+        "ds_read_b64_tr_b16 %2, %9 offset:12288\n"
+        "ds_read_b64_tr_b16 %3, %9 offset:13312\n"
+        "ds_read_b64_tr_b16 %4, %10 offset:12288\n"
+        "ds_read_b64_tr_b16 %5, %10 offset:13312\n"
+        "ds_read_b64_tr_b16 %6, %11 offset:12288\n"
+        "ds_read_b64_tr_b16 %7, %11 offset:13312\n"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3])
         : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]));
   }
 };
 
+template <>
+struct VtFrag<64> {
+  template <int CC>
+  static __device__ __forceinline__ void read(const uint32_t (&addr)[2], s16x4 (&lo)[2],
+                                              s16x4 (&hi)[2]) {
+    if constexpr (CC == 0)
+      asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:0\n"
+        "ds_read_b64_tr_b16 %1, %4 offset:512\n"
+        "ds_read_b64_tr_b16 %2, %5 offset:0\n"
+        "ds_read_b64_tr_b16 %3, %5 offset:512\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
+        : "v"(addr[0]), "v"(addr[1]));
+    else if constexpr (CC == 1)
+      asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:2048\n"
+        "ds_read_b64_tr_b16 %1, %4 offset:2560\n"
+        "ds_read_b64_tr_b16 %2, %5 offset:2048\n"
+        "ds_read_b64_tr_b16 %3, %5 offset:2560\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
+        : "v"(addr[0]), "v"(addr[1]));
+    else if constexpr (CC == 2)
+      asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:4096\n"
+        "ds_read_b64_tr_b16 %1, %4 offset:4608\n"
+        "ds_read_b64_tr_b16 %2, %5 offset:4096\n"
+        "ds_read_b64_tr_b16 %3, %5 offset:4608\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
+        : "v"(addr[0]), "v"(addr[1]));
+    else
+      asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:6144\n"
+        "ds_read_b64_tr_b16 %1, %4 offset:6656\n"
+        "ds_read_b64_tr_b16 %2, %5 offset:6144\n"
+        "ds_read_b64_tr_b16 %3, %5 offset:6656\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
+        : "v"(addr[0]), "v"(addr[1]));
+  }
+};
+
 // grid.x enumerates (sequence, kv head, key split) and grid.y the query tiles, so the tiles that
 // share one K/V panel have ids grid.x apart: with grid.x a multiple of 8 they run on the same XCD
 // and read the panel through one L2.
-#ifndef DLLM_ATTN_WAVES
-#define DLLM_ATTN_WAVES 2
-#endif
-template <int HD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DLLM_ATTN_WAVES, DLLM_ATTN_WAVES)))
+template <int HD, int NW, int ST>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(AttnArgs a) {
-  constexpr int KB = HD / 32;          // 32-wide k-steps of q.k over hd
-  constexpr int HB = HD / 16;          // 16-wide output blocks of hd
-  constexpr int RB = HD * 2;           // bytes per K or V row
-  constexpr int CPR = RB / 16;         // 16-byte chunks per row
-  constexpr int RPI = 1024 / RB;       // rows per DMA wave instruction
-  constexpr int HALF = kTK * RB;       // bytes of the K (or V) rows of one tile
-  constexpr int SLOT = 2 * HALF;       // K rows, then V rows
-  constexpr int PER = SLOT / 1024 / 4;  // DMA instructions per wave per tile (K half, then V half)
-  constexpr int ST = kAttnST;
-  static_assert(ST >= 2 && (ST - 2) * PER < 64, "vmcnt range");
+  constexpr int KK = HD / 16;              // 16-wide k-steps of q.k over hd
+  constexpr int NB = HD / 32;              // 32-wide hd blocks of the output
+  constexpr int RB = HD * 2;               // bytes per K or V row
+  constexpr int CPR = RB / 16;             // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;           // rows per DMA wave instruction
+  constexpr int HALF = kTK * RB;           // bytes of the K (or V) rows of one tile
+  constexpr int SLOT = 2 * HALF;           // K rows, then V rows
+  constexpr int PER = SLOT / 1024 / NW;    // DMA instructions per wave per tile (K half, V half)
+  constexpr int TQ = 32 * NW;              // query rows per workgroup
+  static_assert(PER % 2 == 0 && ST >= 2 && (ST - 2) * PER < 64, "tile shape");
   __shared__ __attribute__((aligned(1024))) char ring[ST * SLOT];
 
   const int G = a.H / a.Hkv;
@@ -190,7 +210,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const int M = min(a.row_ptr[a.B], a.m_cap);
   const int r0 = min(a.row_ptr[b], M), r1 = min(a.row_ptr[b + 1], M);
   const int nrows = (r1 - r0) * G;
-  const int tile0 = blockIdx.y * kTQ;
+  const int tile0 = blockIdx.y * TQ;
   if (tile0 >= nrows) return;
   const int t0 = split * a.kps;
   const int t1 = min(a.S, t0 + a.kps);
@@ -198,54 +218,39 @@ void attn_bf16_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 15, lg = lane >> 4;
+  const int n = lane & 31, h = lane >> 5, g = lane >> 4, q16 = lane & 15;
 
-  // ---- this lane's query rows: column lr of each of the wave's S^T blocks
-  bool qvalid[kQB];
-  int qj[kQB], qh[kQB];
-  bf16x8 qf[kQB][KB];
+  // ---- this lane's query: column n of the wave's 32-query block
+  const int qr = tile0 + 32 * wave + n;
+  const bool qvalid = qr < nrows;
+  const int qj = qvalid ? r0 + qr / G : 0;
+  const int qh = qvalid ? hk * G + qr % G : 0;
+  bf16x8 qf[KK];
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int qr = tile0 + wave * (16 * kQB) + qb * 16 + lr;
-    qvalid[qb] = qr < nrows;
-    qj[qb] = qvalid[qb] ? r0 + qr / G : 0;
-    qh[qb] = qvalid[qb] ? hk * G + qr % G : 0;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      qf[qb][kb] = qvalid[qb] ? *reinterpret_cast<const bf16x8*>(a.q + (size_t)qj[qb] * Nq +
-                                                                 qh[qb] * HD + kb * 32 + lg * 8)
-                              : bf16x8{};
-  }
+  for (int kk = 0; kk < KK; ++kk)
+    qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(a.q + (size_t)qj * Nq + qh * HD + 16 * kk + 8 * h)
+                    : bf16x8{};
 
-  f32x4 oacc[kQB][HB];
+  f32x16 oacc[NB];
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb)
+  for (int hb = 0; hb < NB; ++hb)
 #pragma unroll
-    for (int i = 0; i < HB; ++i) oacc[qb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // m_run: reference point of the exponentials (base-2 units), identical in the 4 lanes that hold
-  // one query; lacc: the sum of the exponentials (all 4 entries, in all 4 lanes of the query)
-  float m_run[kQB];
-  f32x4 lacc[kQB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) { m_run[qb] = -INFINITY; lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-  bf16x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+    for (int i = 0; i < 16; ++i) oacc[hb][i] = 0.f;
+  // m_run: reference point of the exponentials (base-2 units), the same in the two lanes of a
+  // query; l_run: this lane's share (its 32 keys of every tile) of the sum of exponentials
+  float m_run = -INFINITY, l_run = 0.f;
 
   const size_t head_off = ((size_t)b * a.Hkv + hk) * (size_t)a.S * HD;
   const uint16_t* kbase = a.kc + head_off;
   const uint16_t* vbase = a.vc + head_off;
 
-  // ---- direct-to-LDS loads of one tile. DMA instruction p of a wave fills 1 KB = RPI rows of the
-  // K half (p < PER/2) or V half: row = RPI (wave + 4 pp) + lane / CPR, pp = p mod PER/2, chunk
-  // swizzled by the row. The swizzle repeats every 8 RPI rows, so two per-lane byte offsets cover
-  // every pp; the rest of the address is wave-uniform.
-  uint32_t doff[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int rw = RPI * wave + lane / CPR;
-    doff[e] = (uint32_t)(rw * RB + 16 * ((lane % CPR) ^ aswz<CPR>(rw + 4 * RPI * e)));
-  }
+  // ---- direct-to-LDS loads of one tile. DMA instruction p of a wave fills 1 KB block
+  // j = wave + NW pp (pp = p mod PER/2) of the K half (p < PER/2) or of the V half: rows
+  // RPI j + lane/CPR, chunk swizzled by the row. The swizzles do not see the row bits that pp
+  // changes, so one per-lane byte offset per half covers every pp; the rest is wave-uniform.
+  const int rw = RPI * wave + lane / CPR;
+  const uint32_t doff_k = (uint32_t)(rw * RB + 16 * ((lane % CPR) ^ swz_k<CPR>(rw)));
+  const uint32_t doff_v = (uint32_t)(rw * RB + 16 * ((lane % CPR) ^ swz_v<CPR>(rw)));
   auto issue = [&](int it, char* slot) {
     const int tk = t0 + it * kTK;
     if (tk + kTK <= t1) {
@@ -253,9 +258,9 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int p = 0; p < PER; ++p) {
         const bool isk = p < PER / 2;
         const int pp = isk ? p : p - PER / 2;
-        const char* gb = (const char*)((isk ? kbase : vbase) + (size_t)(tk + 4 * RPI * pp) * HD);
-        __builtin_amdgcn_global_load_lds(gb + doff[pp & 1],
-                                         (lds_void_a*)(slot + (isk ? 0 : HALF) + (wave + 4 * pp) * 1024),
+        const char* gb = (const char*)((isk ? kbase : vbase) + (size_t)(tk + RPI * NW * pp) * HD);
+        __builtin_amdgcn_global_load_lds(gb + (isk ? doff_k : doff_v),
+                                         (lds_void_a*)(slot + (isk ? 0 : HALF) + (wave + NW * pp) * 1024),
                                          16, 0, 0);
       }
     } else {  // last tile of a ragged range: rows past it repeat the last key (masked below)
@@ -263,24 +268,28 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int p = 0; p < PER; ++p) {
         const bool isk = p < PER / 2;
         const int pp = isk ? p : p - PER / 2;
-        const int row = RPI * (wave + 4 * pp) + lane / CPR;
+        const int row = RPI * (wave + NW * pp) + lane / CPR;
         const int key = min(tk + row, t1 - 1);
-        const int c = (lane % CPR) ^ aswz<CPR>(row);
+        const int c = (lane % CPR) ^ (isk ? swz_k<CPR>(row) : swz_v<CPR>(row));
         const uint16_t* src = (isk ? kbase : vbase) + (size_t)key * HD + 8 * c;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_a*)(slot + (isk ? 0 : HALF) + (wave + 4 * pp) * 1024),
+        __builtin_amdgcn_global_load_lds(src, (lds_void_a*)(slot + (isk ? 0 : HALF) + (wave + NW * pp) * 1024),
                                          16, 0, 0);
       }
     }
   };
 
-  // V^T fragment addresses relative to the slot: lane q of a 16-lane group reads 4 values of key
-  // row 8 lg + q/4 at hd column 16 hb + 4 (q%4)
-  const int trow = 8 * lg + (lr >> 2);
-  uint32_t voff[HB];
+  // K fragment rows: S^T row n of key block kb2 holds key 32 kb2 + 16 (n/16) + 8 ((n/4)%2) +
+  // 4 ((n/8)%2) + n%4, which puts the scores of chunk cc (16 keys) at accumulator entries
+  // 8 (cc%2) .. 8 (cc%2) + 7 of block cc/2, in k-slot order 8 (lane/32) + i
+  const int kr = 16 * (n >> 4) + 8 * ((n >> 2) & 1) + 4 * ((n >> 3) & 1) + (n & 3);
+  // V^T fragment addresses (relative to the slot): lane q16 of 16-lane group g reads row
+  // 8 (g/2) + q16/4 at hd column 32 hb + 16 (g%2) + 4 (q16%4)
+  const int vr = 8 * (g >> 1) + (q16 >> 2);
+  uint32_t voff[NB];
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int col = 16 * hb + 4 * (lr & 3);
-    voff[hb] = (uint32_t)(HALF + trow * RB + (((col >> 3) ^ aswz<CPR>(trow)) << 4) + (col & 7) * 2);
+  for (int hb = 0; hb < NB; ++hb) {
+    const int col = 32 * hb + 16 * (g & 1) + 4 * (q16 & 3);
+    voff[hb] = (uint32_t)(HALF + vr * RB + (((col >> 3) ^ swz_v<CPR>(vr)) << 4) + (col & 7) * 2);
   }
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
   // a zero scale (uniform attention) runs as a tiny positive one: every exponential is then exactly
@@ -303,151 +312,128 @@ void attn_bf16_kernel(AttnArgs a) {
     const char* sK = ring + slot * SLOT;
     const int tk = t0 + it * kTK;
 
-    // ---- S^T blocks: blk = 2 ks + half, row m <-> key 32 ks + 8 (m/4) + 4 half + m%4
-    f32x4 sacc[kQB][4];
+    // ---- S^T blocks (32 keys x 32 queries)
+    f32x16 sacc[2];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const int ks = blk >> 1, half = blk & 1;
-      const int kr = 32 * ks + 8 * (lr >> 2) + 4 * half + (lr & 3);
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) sacc[qb][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 16; ++i) sacc[kb2][i] = 0.f;
+      const int key = 32 * kb2 + kr;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int ch = (kb * 4 + lg) ^ aswz<CPR>(kr);
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + kr * RB + (ch << 4));
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-          sacc[qb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][kb], sacc[qb][blk],
-                                                                   0, 0, 0);
+      for (int kk = 0; kk < KK; ++kk) {
+        const int ch = (2 * kk + h) ^ swz_k<CPR>(key);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + key * RB + (ch << 4));
+        sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb2], 0, 0, 0);
       }
     }
-    // sacc[qb][blk][i] = raw score q.k of query (qb, lr) with key tk + 32 ks + 8 lg + 4 half + i,
-    // i.e. key offset 32 ks + 4 half + i from tk + 8 lg. On the last tile of a ragged range, keys
-    // past it get the raw score whose scaled value is -inf: they drop out of the maximum and their
-    // exponential is 0.
+    // sacc[kb2][rr] = raw score of query n with key tk + 8 h + koff(kb2, rr),
+    // koff = 32 kb2 + 16 (rr/8) + 4 ((rr/4)%2) + rr%4. On the last tile of a ragged range, keys
+    // past it get the raw score whose scaled value is -inf: they drop out of the maximum and
+    // their exponential is 0.
     if (tk + kTK > t1) {
-      const int rem = t1 - tk - 8 * lg;
+      const int rem = t1 - tk - 8 * h;
       const float excl = c_pos ? -INFINITY : INFINITY;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int qb = 0; qb < kQB; ++qb)
-            if (32 * (blk >> 1) + 4 * (blk & 1) + i >= rem) sacc[qb][blk][i] = excl;
+        for (int rr = 0; rr < 16; ++rr)
+          if (32 * kb2 + 16 * (rr >> 3) + 4 * ((rr >> 2) & 1) + (rr & 3) >= rem) sacc[kb2][rr] = excl;
     }
-    // ---- this lane's maximum of the scaled scores (the scale may be negative). The reference
-    // point moves only when a tile maximum exceeds it by more than kLazy (base-2 units), so the
-    // exponentials stay below 2^kLazy (exact in fp32 and bf16) and the final division by the sum of
-    // the same exponentials cancels the reference. Whether any query of the wave needs a move is
-    // decided from the lanes' own maxima; only then are they reduced across the 4 lanes of a query
-    // and the accumulators rescaled.
-    float lmax[kQB];
-    bool need = false;
+    // ---- lazily moved reference point: it moves only when a tile maximum exceeds it by more
+    // than kLazy, so the exponentials stay below 2^kLazy (exact in fp32 and bf16) and the final
+    // division by the sum of the same exponentials cancels it. Whether any query of the wave needs
+    // a move is decided from the lanes' own maxima; only then are they combined across the two
+    // lanes of a query and the accumulators rescaled.
+    float lmax;
+    if (c_pos) {
+      lmax = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      float m;
-      if (c_pos) {
-        m = fmaxf(fmaxf(sacc[qb][0][0], sacc[qb][0][1]), fmaxf(sacc[qb][0][2], sacc[qb][0][3]));
+      for (int i = 2; i < 16; ++i) lmax = fmaxf(lmax, sacc[0][i]);
 #pragma unroll
-        for (int blk = 1; blk < 4; ++blk)
+      for (int i = 0; i < 16; ++i) lmax = fmaxf(lmax, sacc[1][i]);
+    } else {
+      lmax = fminf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) m = fmaxf(m, sacc[qb][blk][i]);
-      } else {
-        m = fminf(fminf(sacc[qb][0][0], sacc[qb][0][1]), fminf(sacc[qb][0][2], sacc[qb][0][3]));
+      for (int i = 2; i < 16; ++i) lmax = fminf(lmax, sacc[0][i]);
 #pragma unroll
-        for (int blk = 1; blk < 4; ++blk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) m = fminf(m, sacc[qb][blk][i]);
-      }
-      lmax[qb] = m * c;
-      need |= lmax[qb] > m_run[qb] + kLazy;
+      for (int i = 0; i < 16; ++i) lmax = fminf(lmax, sacc[1][i]);
     }
-    if (__any(need)) {
+    lmax *= c;
+    if (__any(lmax > m_run + kLazy)) {
+      const float mx = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
+      const float m_new = (mx > m_run + kLazy) ? mx : m_run;
+      const float alpha = fast_exp2(m_run - m_new);  // 1 if kept; 0 on the first tile
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        float mx = lmax[qb];
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = (mx > m_run[qb] + kLazy) ? mx : m_run[qb];
-        const float alpha = fast_exp2(m_run[qb] - m_new);  // 1 if kept; 0 on the first tile
-        m_run[qb] = m_new;
-        lacc[qb][0] *= alpha; lacc[qb][1] *= alpha; lacc[qb][2] *= alpha; lacc[qb][3] *= alpha;
+      for (int hb = 0; hb < NB; ++hb)
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          oacc[qb][hb][0] *= alpha; oacc[qb][hb][1] *= alpha;
-          oacc[qb][hb][2] *= alpha; oacc[qb][hb][3] *= alpha;
+        for (int i = 0; i < 16; ++i) oacc[hb][i] *= alpha;
+    }
+    bf16x8 pf[4];  // chunk cc: keys 16 cc + 8 h + i8
+    {
+      const float mneg = -m_run;
+      float psum = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int i8 = 0; i8 < 8; ++i8) {
+          const float p = fast_exp2(fmaf(sacc[cc >> 1][8 * (cc & 1) + i8], c, mneg));
+          psum += p;
+          pf[cc][i8] = (__bf16)p;
         }
-      }
+      l_run += psum;
     }
-    bf16x8 pf[kQB][2];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float mneg = -m_run[qb];
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pf[qb][blk >> 1][4 * (blk & 1) + i] = (__bf16)fast_exp2(fmaf(sacc[qb][blk][i], c, mneg));
-    }
-    // ---- O^T += V^T P^T: A operand row = hd column, k-slot s = key 32 ks + 8 lg + s
+    // ---- O^T += V^T P^T, 16 keys per product
     const uint32_t vslot = ring_lds + slot * SLOT;
-    uint32_t addr[HB];
+    uint32_t addr[NB];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) addr[hb] = vslot + voff[hb];
-    auto pv = [&](auto ks_c) {
-      constexpr int ks = decltype(ks_c)::value;
-      s16x4 lo[HB], hi[HB];
-      VtFrag<HD>::template read<ks>(addr, lo, hi);
+    for (int hb = 0; hb < NB; ++hb) addr[hb] = vslot + voff[hb];
+    auto pv = [&](auto cc_c) {
+      constexpr int cc = decltype(cc_c)::value;
+      s16x4 lo[NB], hi[NB];
+      VtFrag<HD>::template read<cc>(addr, lo, hi);
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
+      for (int hb = 0; hb < NB; ++hb) {
         typedef short __attribute__((ext_vector_type(8))) s16x8;
         const s16x8 both = {lo[hb][0], lo[hb][1], lo[hb][2], lo[hb][3],
                             hi[hb][0], hi[hb][1], hi[hb][2], hi[hb][3]};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-          oacc[qb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb][ks], oacc[qb][hb],
-                                                                  0, 0, 0);
+        oacc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf[cc],
+                                                            oacc[hb], 0, 0, 0);
       }
     };
     pv(std::integral_constant<int, 0>{});
     pv(std::integral_constant<int, 1>{});
-    // sums of the same (bf16) probabilities: an all-ones A operand makes every row of the product
-    // the column sum, so each lane receives its query's complete sum
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][0], lacc[qb], 0, 0, 0);
-      lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][1], lacc[qb], 0, 0, 0);
-    }
+    pv(std::integral_constant<int, 2>{});
+    pv(std::integral_constant<int, 3>{});
   }
 
-  // oacc[qb][hb][i] = unnormalised o[query (qb, lr)][hd = 16 hb + 4 lg + i]; lacc holds the
-  // query's complete sum
+  // oacc[hb][rr] = unnormalised o[query n][hd 32 hb + 8 (rr/4) + 4 h + rr%4]
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!qvalid) return;
+  if (a.nsplit == 1) {
+    const float inv = 1.0f / l_tot;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const float l_tot = lacc[qb][0];
-    if (!qvalid[qb]) continue;
-    const int j = qj[qb], h = qh[qb];
-    if (a.nsplit == 1) {
-      const float inv = 1.0f / l_tot;
+    for (int hb = 0; hb < NB; ++hb)
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const float v[4] = {oacc[qb][hb][0] * inv, oacc[qb][hb][1] * inv, oacc[qb][hb][2] * inv,
-                            oacc[qb][hb][3] * inv};
-        Elem<uint16_t>::store4(a.o + (size_t)j * Nq + h * HD + hb * 16 + 4 * lg, v);
+      for (int jj = 0; jj < 4; ++jj) {
+        const float v[4] = {oacc[hb][4 * jj] * inv, oacc[hb][4 * jj + 1] * inv,
+                            oacc[hb][4 * jj + 2] * inv, oacc[hb][4 * jj + 3] * inv};
+        Elem<uint16_t>::store4(a.o + (size_t)qj * Nq + qh * HD + 32 * hb + 8 * jj + 4 * h, v);
       }
-    } else {
-      const size_t base = ((size_t)split * a.m_cap + j) * a.H + h;
+  } else {
+    const size_t base = ((size_t)split * a.m_cap + qj) * a.H + qh;
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const float v[4] = {oacc[qb][hb][0], oacc[qb][hb][1], oacc[qb][hb][2], oacc[qb][hb][3]};
-        Elem<float>::store4(a.part_o + base * HD + hb * 16 + 4 * lg, v);
+    for (int hb = 0; hb < NB; ++hb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float v[4] = {oacc[hb][4 * jj], oacc[hb][4 * jj + 1], oacc[hb][4 * jj + 2],
+                            oacc[hb][4 * jj + 3]};
+        Elem<float>::store4(a.part_o + base * HD + 32 * hb + 8 * jj + 4 * h, v);
       }
-      if (lg == 0) {
-        a.part_ml[base * 2] = m_run[qb];
-        a.part_ml[base * 2 + 1] = l_tot;
-      }
+    if (h == 0) {
+      a.part_ml[base * 2] = m_run;
+      a.part_ml[base * 2 + 1] = l_tot;
     }
   }
 }
@@ -529,30 +515,50 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgsF32 a) {
 // ---------------------------------------------------------------- host side
 static inline int cdiv(long x, long y) { return (int)((x + y - 1) / y); }
 
-static void split_keys(bool bf16, const ProjShape& s, int& nsplit, int& kps) {
-  nsplit = 1;
-  if (bf16) {
-    const int G = s.H / s.Hkv;
-    const long est = (long)(cdiv((long)s.m_cap * G, kTQ) > 0 ? cdiv((long)s.m_cap * G, kTQ) : 1) *
-                     s.Hkv;
-    while (est * nsplit < 512 && s.S / (nsplit * 2) >= 128) nsplit *= 2;
-  }
-  kps = cdiv(cdiv(s.S, nsplit), kTK) * kTK;
-  nsplit = cdiv(s.S, kps);  // every split owns at least one key
+// bf16 launch plan: waves per workgroup (32 query rows each) and the key split. Eight waves
+// (256 rows, one workgroup per CU, 4-deep ring) when a (sequence, kv head) has more than 160 query
+// rows on average, else four (128 rows, two workgroups per CU). The key range is split until the
+// workgroups fill every CU slot, keeping at least 128 keys per split.
+struct AttnCfg {
+  int nw, st, nsplit, kps;
+};
+static AttnCfg plan_bf16(const ProjShape& s) {
+  AttnCfg c;
+  const int G = s.H / s.Hkv;
+  const long rows_avg = (long)cdiv((long)s.m_cap * G, s.B);
+  c.nw = rows_avg > 160 ? 8 : 4;
+#ifdef DLLM_ATTN_FORCE_NW
+  c.nw = DLLM_ATTN_FORCE_NW;
+#endif
+  c.st = (c.nw == 8 || s.hd == 64) ? 4 : 2;
+  const long slots = 256L * (c.nw == 8 ? 1 : 2);
+  const long est = (long)s.B * s.Hkv * (rows_avg > 0 ? cdiv(rows_avg, 32 * c.nw) : 1);
+  c.nsplit = 1;
+  while (est * c.nsplit < slots && s.S / (c.nsplit * 2) >= 128) c.nsplit *= 2;
+  c.kps = cdiv(cdiv(s.S, c.nsplit), kTK) * kTK;
+  c.nsplit = cdiv(s.S, c.kps);  // every split owns at least one key
+  return c;
 }
 
 AttnPlan plan_attn(bool bf16, const ProjShape& s) {
-  int n, k;
-  split_keys(bf16, s, n, k);
-  return AttnPlan{n};
+  return AttnPlan{bf16 ? plan_bf16(s).nsplit : 1};
 }
 
 size_t attn_workspace_bytes(bool bf16, const ProjShape& s) {
-  int nsplit, kps;
-  split_keys(bf16, s, nsplit, kps);
-  if (nsplit <= 1) return 0;
-  const size_t rows = (size_t)nsplit * s.m_cap * s.H;
+  if (!bf16) return 0;
+  const AttnCfg c = plan_bf16(s);
+  if (c.nsplit <= 1) return 0;
+  const size_t rows = (size_t)c.nsplit * s.m_cap * s.H;
   return ((rows * s.hd * 4 + 255) & ~(size_t)255) + rows * 2 * 4;
+}
+
+template <int HD>
+static void launch_bf16(const AttnCfg& c, dim3 grid, const AttnArgs& a, hipStream_t st) {
+  constexpr int ST4 = HD == 64 ? 4 : 2;  // ring depth of the four-wave variant (two per CU)
+  if (c.nw == 8)
+    hipLaunchKernelGGL((attn_bf16_kernel<HD, 8, 4>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<HD, 4, ST4>), grid, dim3(256), 0, st, a);
 }
 
 hipError_t launch_attn(bool bf16, const ProjShape& s, float scale, const void* q_sel,
@@ -569,11 +575,12 @@ hipError_t launch_attn(bool bf16, const ProjShape& s, float scale, const void* q
       hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(256), 0, st, f);
     return hipGetLastError();
   }
+  const AttnCfg c = plan_bf16(s);
   AttnArgs a;
   a.q = (const uint16_t*)q_sel; a.kc = (const uint16_t*)k_cache; a.vc = (const uint16_t*)v_cache;
   a.row_ptr = row_ptr; a.o = (uint16_t*)o_sel;
   a.B = s.B; a.S = s.S; a.H = s.H; a.Hkv = s.Hkv; a.m_cap = s.m_cap;
-  split_keys(true, s, a.nsplit, a.kps);
+  a.nsplit = c.nsplit; a.kps = c.kps;
   a.scale_log2 = scale * kLog2e;
   a.part_o = nullptr; a.part_ml = nullptr;
   if (a.nsplit > 1) {
@@ -583,11 +590,11 @@ hipError_t launch_attn(bool bf16, const ProjShape& s, float scale, const void* q
   }
   const int G = s.H / s.Hkv;
   const int rows_max = (s.m_cap < s.S ? s.m_cap : s.S) * G;
-  dim3 grid(s.B * s.Hkv * a.nsplit, cdiv(rows_max, kTQ));
+  dim3 grid(s.B * s.Hkv * a.nsplit, cdiv(rows_max, 32 * c.nw));
   if (s.hd == 64)
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, st, a);
+    launch_bf16<64>(c, grid, a, st);
   else
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, st, a);
+    launch_bf16<128>(c, grid, a, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const size_t threads = (size_t)s.m_cap * s.H * (s.hd / 4);
