@@ -14,13 +14,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 // ---------------------------------------------------------------------------------- bf16 <-> f32
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// round-to-nearest-even float -> bf16 bits; NaN stays NaN (quiet)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// round-to-nearest-even float -> bf16 bits (the gfx950 conversion instruction, two at a time);
+// NaN stays NaN (quiet)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
+__device__ __forceinline__ uint16_t f2bf(float f) { return (uint16_t)f2bf2(f, 0.f); }
 
 // storage-type traits: load/store 4 or 8 consecutive elements as float
 template <typename T> struct Elem;
@@ -59,8 +60,8 @@ template <> struct Elem<uint16_t> {  // bf16 bit patterns
   }
   __device__ __forceinline__ static void store4(uint16_t* p, const float v[4]) {
     uint2 a;
-    a.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    a.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    a.x = f2bf2(v[0], v[1]);
+    a.y = f2bf2(v[2], v[3]);
     *reinterpret_cast<uint2*>(p) = a;
   }
   __device__ __forceinline__ static float load1(const uint16_t* p) { return bf2f(*p); }

@@ -7,17 +7,17 @@
 // Every projection is a dense contraction C[M, N] = X[M, K] W[N, K]^T of the M selected rows
 // (compacted to consecutive rows by a gather/RMSNorm pass) with a weight stored [out, in].
 // Both operands are K-contiguous, which is the operand layout of the bf16 matrix-core
-// instruction v_mfma_f32_16x16x32_bf16: a lane supplies 8 consecutive K values of one row.
-// The kernel multiplies W (instruction A operand, rows = output columns n) by X (B operand,
-// rows = tokens m), so each lane's 4 accumulators are 4 CONSECUTIVE output columns of one
-// token row: every epilogue stores 8 or 16 contiguous bytes per lane straight into its target
-// (q rows, K/V cache rows of the token's position, residual rows, scattered hidden rows).
+// instructions: a lane supplies 8 consecutive K values of one row. The kernels multiply W
+// (instruction A operand, rows = output columns n) by X (B operand, rows = tokens m), so each
+// lane's accumulators are groups of 4 CONSECUTIVE output columns of one token row: every
+// epilogue stores 8 or 16 contiguous bytes per lane straight into its target (q rows, K/V cache
+// rows of the token's position, residual rows, scattered hidden rows).
 //
-// Tiles: BM (64|128) tokens x 128 weight rows x 64 K per step, 256 threads = 2 x 2 waves.
-// Global -> register prefetch of the next K step overlaps the MFMAs of the current one; LDS rows
-// are padded to 144 bytes so the 16 lanes reading one 16-row fragment hit distinct banks.
-// At small M the GEMMs stream weights (HBM-bound); a few K splits fill the 256 CUs and are
-// reduced in a fixed order by a second pass (deterministic).
+// Operands reach LDS through a ring of direct-to-LDS loads. Up to 128 selected rows the products
+// stream the weights (HBM-bound) with 16 x 16 x 32 blocks and narrow weight slabs, a few K splits
+// filling the 256 CUs and reduced in a fixed order by a second pass (deterministic). Above that
+// the products are compute-bound and use 32 x 32 x 16 blocks, which sustain about twice the
+// matrix-core rate of 16 x 16 x 32 on gfx950, in 256-row tiles.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,28 +26,53 @@ namespace dllm {
 // =========================================================================================
 // epilogues: apply to 4 consecutive columns n..n+3 of compact row j (n % 4 == 0)
 // =========================================================================================
+// Epilogues: row(j) prepares what depends on the compact row j only (called once per row and
+// thread), operator() applies to 4 consecutive columns n..n+3 of that row (n % 4 == 0).
+
+// quotient n / d for 0 <= n < 2^31 by multiply-high (round-up method, exact in this range)
+struct FastDiv {
+  uint32_t m, l, d;
+  static FastDiv make(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    f.l = 0;
+    while ((1ull << f.l) < d) ++f.l;
+    f.m = (uint32_t)(((1ull << 32) * ((1ull << f.l) - d)) / d + 1);
+    return f;
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const { return (__umulhi(m, n) + n) >> l; }
+};
+
 template <typename T>
 struct EpiQKV {  // Q -> q_sel[j]; K/V -> cache[b, hk, s, e] of the token's own position
   T* q_sel;
   T* kc;
   T* vc;
   const int32_t* sel_idx;
-  int Nq, Nkv, hd, S, Hkv;
-  __device__ __forceinline__ void operator()(int j, int n, const float v[4]) const {
+  int Nq, Nkv, hd_log2, S, Hkv;
+  FastDiv divS;
+  struct Row {
+    T* q;       // q_sel row j
+    size_t kv;  // element offset of cache[b, 0, s, 0]
+  };
+  __device__ __forceinline__ Row row(int j) const {
+    const uint32_t id = (uint32_t)sel_idx[j];
+    const uint32_t b = divS.div(id), s = id - b * (uint32_t)S;
+    return Row{q_sel + (size_t)j * Nq, ((size_t)b * Hkv * S + s) << hd_log2};
+  }
+  __device__ __forceinline__ void operator()(const Row& r, int n, const float v[4]) const {
     if (n < Nq) {
-      Elem<T>::store4(q_sel + (size_t)j * Nq + n, v);
+      Elem<T>::store4(r.q + n, v);
       return;
     }
-    const int id = sel_idx[j];
-    const int b = id / S, s = id - (id / S) * S;
     int kv = n - Nq;
     T* cache = kc;
     if (kv >= Nkv) {
       kv -= Nkv;
       cache = vc;
     }
-    const int hk = kv / hd, e = kv - hk * hd;
-    Elem<T>::store4(cache + (((size_t)b * Hkv + hk) * S + s) * hd + e, v);
+    const int hk = kv >> hd_log2, e = kv & ((1 << hd_log2) - 1);
+    Elem<T>::store4(cache + r.kv + (((size_t)hk * S) << hd_log2) + e, v);
   }
 };
 
@@ -57,11 +82,18 @@ struct EpiResidF32 {  // h[j] = h_in[sel[j]] + acc  (float32 workspace)
   const T* x;
   const int32_t* sel_idx;
   int d;
-  __device__ __forceinline__ void operator()(int j, int n, const float v[4]) const {
-    float r[4];
-    Elem<T>::load4(x + (size_t)sel_idx[j] * d + n, r);
-    const float o[4] = {v[0] + r[0], v[1] + r[1], v[2] + r[2], v[3] + r[3]};
-    Elem<float>::store4(h + (size_t)j * d + n, o);
+  struct Row {
+    float* h;
+    const T* x;
+  };
+  __device__ __forceinline__ Row row(int j) const {
+    return Row{h + (size_t)j * d, x + (size_t)sel_idx[j] * d};
+  }
+  __device__ __forceinline__ void operator()(const Row& r, int n, const float v[4]) const {
+    float a[4];
+    Elem<T>::load4(r.x + n, a);
+    const float o[4] = {v[0] + a[0], v[1] + a[1], v[2] + a[2], v[3] + a[3]};
+    Elem<float>::store4(r.h + n, o);
   }
 };
 
@@ -71,11 +103,18 @@ struct EpiResidScatter {  // h_out[sel[j]] = h[j] + acc
   const float* h;
   const int32_t* sel_idx;
   int d;
-  __device__ __forceinline__ void operator()(int j, int n, const float v[4]) const {
-    float r[4];
-    Elem<float>::load4(h + (size_t)j * d + n, r);
-    const float o[4] = {v[0] + r[0], v[1] + r[1], v[2] + r[2], v[3] + r[3]};
-    Elem<T>::store4(h_out + (size_t)sel_idx[j] * d + n, o);
+  struct Row {
+    T* out;
+    const float* h;
+  };
+  __device__ __forceinline__ Row row(int j) const {
+    return Row{h_out + (size_t)sel_idx[j] * d, h + (size_t)j * d};
+  }
+  __device__ __forceinline__ void operator()(const Row& r, int n, const float v[4]) const {
+    float a[4];
+    Elem<float>::load4(r.h + n, a);
+    const float o[4] = {v[0] + a[0], v[1] + a[1], v[2] + a[2], v[3] + a[3]};
+    Elem<T>::store4(r.out + n, o);
   }
 };
 
@@ -83,12 +122,14 @@ template <typename T>
 struct EpiSwiGLU {  // z[j, n] = silu(gate) * up
   T* z;
   int F;
-  __device__ __forceinline__ void operator()(int j, int n, const float g[4],
+  typedef T* Row;
+  __device__ __forceinline__ Row row(int j) const { return z + (size_t)j * F; }
+  __device__ __forceinline__ void operator()(Row r, int n, const float g[4],
                                              const float u[4]) const {
     float o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = g[i] / (1.0f + __expf(-g[i])) * u[i];
-    Elem<T>::store4(z + (size_t)j * F + n, o);
+    for (int i = 0; i < 4; ++i) o[i] = __fdividef(g[i], 1.0f + __expf(-g[i])) * u[i];
+    Elem<T>::store4(r + n, o);
   }
 };
 
@@ -147,6 +188,17 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const Tin* in, const 
 // LDS once. Narrow N (4096) uses BN = 64 and a few K splits. At larger M, 128 x 128 tiles with
 // 2 x 2 waves.
 constexpr int kBK = 64;
+
+// Tiles of the 32 x 32 x 16 kernel used when more than 128 rows are selected (measured on MI355X
+// at the LLaDA-8B shapes): 256 x 256 tiles with 32-wide K slots for many rows (8192), 256 x 128
+// tiles with 64-wide slots for a few thousand (1640), where the larger tile count balances better.
+// Both run 8 waves as 4 x 2 (wave tiles 64 x 128 and 64 x 64).
+struct G32Shape {
+  int bm, bn, bk, wm, wn, st;
+};
+constexpr G32Shape kG32Big{256, 256, 32, 4, 2, 4};
+constexpr G32Shape kG32Mid{256, 128, 64, 4, 2, 3};
+constexpr int kG32BigRows = 4096;  // selected rows from which the big tile is used
 
 // ring slots that fit in the 160 KB of LDS a workgroup may use, capped at `want`
 constexpr int ring_slots(int bm, int bn, int bk, int want) {
@@ -312,6 +364,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g, Epi
   for (int i = 0; i < MB; ++i) {
     const int m = m0 + wm * WTM + 16 * i + lr;
     if (m >= M) continue;
+    const auto er = epi.row(m);
     if constexpr (SWIGLU) {
 #pragma unroll
       for (int j = 0; j < NB / 2; ++j) {
@@ -325,7 +378,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g, Epi
           Elem<float>::store4(pr + n, gv);
           Elem<float>::store4(pr + g.N + n, uv);
         } else {
-          epi(m, n, gv, uv);
+          epi(er, n, gv, uv);
         }
       }
     } else {
@@ -337,7 +390,172 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g, Epi
         if (g.partial)
           Elem<float>::store4(g.partial + ((size_t)blockIdx.z * g.m_cap + m) * g.N + n, v);
         else
-          epi(m, n, v);
+          epi(er, n, v);
+      }
+    }
+  }
+}
+
+// Same ring, 32 x 32 x 16 products (about twice the sustained rate of 16 x 16 x 32 on gfx950).
+// A lane supplies 8 consecutive K values (k-step half lane/32) of row lane%32 of a 32-row
+// fragment; its 16 accumulators of a block are C^T[n = 8 (r/4) + 4 (lane/32) + r%4][m = lane%32],
+// i.e. 4 groups of 4 consecutive output columns of one token row. Chunk swizzle for rows of CPR
+// 16-byte chunks: the 16 rows read by a quarter-wave (one chunk each) land on 16 distinct bank
+// positions of the 256 bank bytes.
+template <int CPR>
+__device__ __forceinline__ int swz32(int r) {
+  if constexpr (CPR == 4) return (r >> 2) & 3;
+  else if constexpr (CPR == 8) return (r >> 1) & 7;
+  else return r & 15;
+}
+
+template <int BM, int BN, int BK, int NW, bool SWIGLU>
+__device__ __forceinline__ void issue_stage32(const GemmArgs& g, char* slot, int m0, int n0, int M,
+                                              int k0, int wave, int lane) {
+  constexpr int RB = BK * 2;         // bytes per row
+  constexpr int CPR = RB / 16;       // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;     // rows per wave instruction
+  constexpr int I = (BM + BN) / RPI; // wave instructions per slot
+  constexpr int PER = (I + NW - 1) / NW;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = wave + NW * i;
+    if (I % NW == 0 || j < I) {
+      const int row = RPI * j + lane / CPR;
+      const int c = (lane % CPR) ^ swz32<CPR>(row);
+      const uint16_t* src;
+      if (row < BM) {
+        src = g.X + (size_t)min(m0 + row, M - 1) * g.K;
+      } else {
+        const int r = row - BM;
+        if constexpr (SWIGLU) {
+          const int n = min(n0 + (r % (BN / 2)), g.N - 1);
+          src = ((r < BN / 2) ? g.W : g.W2) + (size_t)n * g.K;
+        } else {
+          src = g.W + (size_t)min(n0 + r, g.N - 1) * g.K;
+        }
+      }
+      __builtin_amdgcn_global_load_lds(src + k0 + 8 * c, (lds_void*)(slot + j * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// first W row (within the W part of the slot) of the wave's 32-row n-block j
+template <int BN, int WN, int NB, bool SWIGLU>
+__device__ __forceinline__ int wrow32(int wn, int j) {
+  if constexpr (SWIGLU) {
+    constexpr int HW = BN / 2 / WN;  // gate rows per wave
+    return (j < NB / 2) ? wn * HW + 32 * j : BN / 2 + wn * HW + 32 * (j - NB / 2);
+  } else {
+    return wn * (BN / WN) + 32 * j;
+  }
+}
+
+template <int BK>
+__device__ __forceinline__ bf16x8 frag32(const char* slot, int row, int chunk) {
+  constexpr int RB = BK * 2;
+  return *reinterpret_cast<const bf16x8*>(slot + row * RB + ((chunk ^ swz32<RB / 16>(row)) << 4));
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int BM, int BN, int BK, int WM, int WN, int ST, bool SWIGLU, class Epi>
+__global__ __launch_bounds__(64 * WM * WN) void gemm32_bf16_kernel(GemmArgs g, Epi epi) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MB = WTM / 32, NB = WTN / 32;
+  constexpr int SLOT = (BM + BN) * BK * 2;
+  constexpr int NMIN = (BM + BN) * BK * 2 / 1024 / NW;  // DMA instructions per wave per slot (lower bound)
+  static_assert(MB >= 1 && NB >= 1 && (!SWIGLU || NB % 2 == 0), "tile");
+  static_assert(ST >= 3 && (ST - 2) * NMIN < 64 && NMIN >= 1, "ring depth");
+  __shared__ __attribute__((aligned(1024))) char ring[ST * SLOT];
+
+  const int M = live_rows(g.row_ptr, g.B, g.m_cap);
+  const int m0 = blockIdx.y * BM;
+  if (m0 >= M) return;
+  const int n0 = blockIdx.x * (SWIGLU ? BN / 2 : BN);
+  const int kb = blockIdx.z * g.kchunk;
+  const int nk = (min(g.K, kb + g.kchunk) - kb) / BK;  // >= 1 by the plan
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nk)
+      issue_stage32<BM, BN, BK, NW, SWIGLU>(g, ring + s * SLOT, m0, n0, M, kb + s * BK, wave, lane);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_batches<NMIN, ST - 2>(nk - 1 - kt);  // slots issued after slot kt: min(ST-2, nk-1-kt)
+    wg_barrier();
+    if (kt + ST - 1 < nk)
+      issue_stage32<BM, BN, BK, NW, SWIGLU>(g, ring + ((kt + ST - 1) % ST) * SLOT, m0, n0, M,
+                                            kb + (kt + ST - 1) * BK, wave, lane);
+    const char* slot = ring + (kt % ST) * SLOT;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 xf[MB], wf[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) xf[i] = frag32<BK>(slot, wm * WTM + 32 * i + l32, 2 * kk + h);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        wf[j] = frag32<BK>(slot, BM + wrow32<BN, WN, NB, SWIGLU>(wn, j) + l32, 2 * kk + h);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // acc[i][j][4 q + r] = C[m = m0 + wm WTM + 32 i + l32][n = n0 + (n-block j) + 8 q + 4 h + r]
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + wm * WTM + 32 * i + l32;
+    if (m >= M) continue;
+    const auto er = epi.row(m);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < NB / 2; ++j) {
+          const int n = n0 + wrow32<BN, WN, NB, true>(wn, j) + 8 * q + 4 * h;
+          if (n >= g.N) continue;
+          const float gv[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                               acc[i][j][4 * q + 3]};
+          const int ju = j + NB / 2;
+          const float uv[4] = {acc[i][ju][4 * q], acc[i][ju][4 * q + 1], acc[i][ju][4 * q + 2],
+                               acc[i][ju][4 * q + 3]};
+          if (g.partial) {  // [split][row][gate 0..N | up N..2N]
+            float* pr = g.partial + ((size_t)blockIdx.z * g.m_cap + m) * (2 * (size_t)g.N);
+            Elem<float>::store4(pr + n, gv);
+            Elem<float>::store4(pr + g.N + n, uv);
+          } else {
+            epi(er, n, gv, uv);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int n = n0 + wrow32<BN, WN, NB, false>(wn, j) + 8 * q + 4 * h;
+          if (n >= g.N) continue;
+          const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                              acc[i][j][4 * q + 3]};
+          if (g.partial)
+            Elem<float>::store4(g.partial + ((size_t)blockIdx.z * g.m_cap + m) * g.N + n, v);
+          else
+            epi(er, n, v);
+        }
       }
     }
   }
@@ -362,7 +580,7 @@ __global__ __launch_bounds__(256) void splitk_swiglu_kernel(const float* partial
     Elem<float>::load4(pr + N + n, b);
     for (int e = 0; e < 4; ++e) { gv[e] += a[e]; uv[e] += b[e]; }
   }
-  epi(m, n, gv, uv);
+  epi(epi.row(m), n, gv, uv);
 }
 
 // fixed-order sum of the K-split partials, then the epilogue
@@ -382,7 +600,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* partial
     Elem<float>::load4(partial + ((size_t)z * m_cap + m) * N + n, p);
     v[0] += p[0]; v[1] += p[1]; v[2] += p[2]; v[3] += p[3];
   }
-  epi(m, n, v);
+  epi(epi.row(m), n, v);
 }
 
 // =========================================================================================
@@ -455,9 +673,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF32 g, Epi epi) {
     const int m = m0 + ty * 4 + i;
     if (m >= M) continue;
     if constexpr (SWIGLU)
-      epi(m, n, acc[i], accu[i]);
+      epi(epi.row(m), n, acc[i], accu[i]);
     else
-      epi(m, n, acc[i]);
+      epi(epi.row(m), n, acc[i]);
   }
 }
 
@@ -478,8 +696,9 @@ GemmPlan plan_gemm(bool bf16, int m_cap, int N, int K, bool swiglu) {
   GemmPlan p{64, 64, 64, 4, 1, 4, 1};
   if (!bf16) return p;
   if (m_cap > 128) {
-    p = GemmPlan{128, 128, 64, 2, 2, 3, 1};
-    const long tiles = (long)cdiv(N, swiglu ? 64 : 128) * cdiv(m_cap, 128);
+    const G32Shape t = m_cap >= kG32BigRows ? kG32Big : kG32Mid;
+    p = GemmPlan{t.bm, t.bn, t.bk, t.wm, t.wn, t.st, 1, 32};
+    const long tiles = (long)cdiv(N, swiglu ? p.bn / 2 : p.bn) * cdiv(m_cap, p.bm);
     if (!swiglu)
       while (tiles * p.splits < 256 && K / (p.splits * 2) >= 512 && p.splits < 8) p.splits *= 2;
     return p;
@@ -542,6 +761,16 @@ static bool launch_if(const GemmPlan& p, const GemmArgs& g, dim3 grid, Epi epi, 
   }
 }
 
+template <int BM, int BN, int BK, int WM, int WN, int ST, bool SWIGLU, class Epi>
+static bool launch32_if(const GemmPlan& p, const GemmArgs& g, dim3 grid, Epi epi, hipStream_t st) {
+  if (p.mfma != 32 || p.bm != BM || p.bn != BN || p.bk != BK || p.wm != WM || p.wn != WN ||
+      p.st != ST)
+    return false;
+  hipLaunchKernelGGL((gemm32_bf16_kernel<BM, BN, BK, WM, WN, ST, SWIGLU, Epi>), grid,
+                     dim3(64 * WM * WN), 0, st, g, epi);
+  return true;
+}
+
 template <bool SWIGLU, class Epi>
 static hipError_t run_gemm_bf16(const GemmPlan& p, const uint16_t* X, const uint16_t* W,
                                 const uint16_t* W2, int N, int K, const int32_t* row_ptr, int B,
@@ -557,15 +786,21 @@ static hipError_t run_gemm_bf16(const GemmPlan& p, const uint16_t* X, const uint
 #define RS(bm, bn) ring_slots(bm, bn, 64, 4)
   bool ok;
   if constexpr (SWIGLU) {
-    ok = launch_if<128, 96, 64, 4, 1, RS(128, 96), true>(p, g, grid, epi, st) ||
-         launch_if<64, 96, 64, 2, 1, RS(64, 96), true>(p, g, grid, epi, st) ||
-         launch_if<128, 128, 64, 2, 2, 3, true>(p, g, grid, epi, st);
+    ok = launch32_if<kG32Big.bm, kG32Big.bn, kG32Big.bk, kG32Big.wm, kG32Big.wn, kG32Big.st, true>(
+             p, g, grid, epi, st) ||
+         launch32_if<kG32Mid.bm, kG32Mid.bn, kG32Mid.bk, kG32Mid.wm, kG32Mid.wn, kG32Mid.st, true>(
+             p, g, grid, epi, st) ||
+         launch_if<128, 96, 64, 4, 1, RS(128, 96), true>(p, g, grid, epi, st) ||
+         launch_if<64, 96, 64, 2, 1, RS(64, 96), true>(p, g, grid, epi, st);
   } else {
-    ok = launch_if<128, 48, 64, 4, 1, RS(128, 48), false>(p, g, grid, epi, st) ||
+    ok = launch32_if<kG32Big.bm, kG32Big.bn, kG32Big.bk, kG32Big.wm, kG32Big.wn, kG32Big.st, false>(
+             p, g, grid, epi, st) ||
+         launch32_if<kG32Mid.bm, kG32Mid.bn, kG32Mid.bk, kG32Mid.wm, kG32Mid.wn, kG32Mid.st, false>(
+             p, g, grid, epi, st) ||
+         launch_if<128, 48, 64, 4, 1, RS(128, 48), false>(p, g, grid, epi, st) ||
          launch_if<128, 64, 64, 4, 1, RS(128, 64), false>(p, g, grid, epi, st) ||
          launch_if<64, 48, 64, 2, 1, RS(64, 48), false>(p, g, grid, epi, st) ||
-         launch_if<64, 64, 64, 2, 1, RS(64, 64), false>(p, g, grid, epi, st) ||
-         launch_if<128, 128, 64, 2, 2, 3, false>(p, g, grid, epi, st);
+         launch_if<64, 64, 64, 2, 1, RS(64, 64), false>(p, g, grid, epi, st);
   }
 #undef RS
   if (!ok) return hipErrorInvalidConfiguration;
@@ -603,7 +838,9 @@ static hipError_t qkv_impl(const ProjShape& s, const T* h_in, const T* g_attn, c
                      g_attn, xn, s.d, s.eps, row_ptr, s.B, s.m_cap);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  EpiQKV<T> epi{q_sel, kc, vc, sel_idx, Nq, Nkv, s.hd, s.S, s.Hkv};
+  int hd_log2 = 0;
+  while ((1 << hd_log2) < s.hd) ++hd_log2;  // hd is 64 or 128
+  EpiQKV<T> epi{q_sel, kc, vc, sel_idx, Nq, Nkv, hd_log2, s.S, s.Hkv, FastDiv::make((uint32_t)s.S)};
   if constexpr (kBf16) {
     GemmPlan p = plan_gemm(true, s.m_cap, N, s.d, false);
     return run_gemm_bf16<false>(p, xn, w_qkv, nullptr, N, s.d, row_ptr, s.B, s.m_cap, partial,

@@ -46,6 +46,7 @@ struct GemmPlan {
   int wm, wn;  // wave grid
   int st;      // ring slots
   int splits;  // K partitions reduced in a second pass (1 = fused epilogue)
+  int mfma = 16;  // matrix-core block edge: 16 (16x16x32) or 32 (32x32x16)
 };
 // N = output columns (SwiGLU: F, the tile then holds gate and up rows of the same columns)
 GemmPlan plan_gemm(bool bf16, int m_cap, int N, int K, bool swiglu);
