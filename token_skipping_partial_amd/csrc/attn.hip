@@ -297,23 +297,9 @@ void attn_bf16_kernel(AttnArgs a) {
   const float c = a.scale_log2 != 0.f ? a.scale_log2 : 1e-30f;
   const bool c_pos = c > 0.f;
 
-#pragma unroll
-  for (int s = 0; s < ST - 1; ++s)
-    if (s < ntile) issue(s, ring + s * SLOT);
-
-  for (int it = 0; it < ntile; ++it) {
-    const int ahead = min(ST - 2, ntile - 1 - it);  // tiles issued after tile it
-    if (ST > 3 && ahead >= 2) attn_wait_vm<(ST > 3 ? 2 : 0) * PER>();
-    else if (ST > 2 && ahead == 1) attn_wait_vm<PER>();
-    else attn_wait_vm<0>();
-    asm volatile("s_barrier" ::: "memory");  // tile it landed everywhere; slot of it-1 is free
-    if (it + ST - 1 < ntile) issue(it + ST - 1, ring + ((it + ST - 1) % ST) * SLOT);
-    const int slot = it % ST;
-    const char* sK = ring + slot * SLOT;
-    const int tk = t0 + it * kTK;
-
-    // ---- S^T blocks (32 keys x 32 queries)
-    f32x16 sacc[2];
+  static_assert(ST == 4, "the pipelined loop below assumes a 4-slot ring");
+  // ---- S^T blocks (32 keys x 32 queries) of the tile in slot `sK`
+  auto scores = [&](const char* sK, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
@@ -326,10 +312,12 @@ void attn_bf16_kernel(AttnArgs a) {
         sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb2], 0, 0, 0);
       }
     }
-    // sacc[kb2][rr] = raw score of query n with key tk + 8 h + koff(kb2, rr),
-    // koff = 32 kb2 + 16 (rr/8) + 4 ((rr/4)%2) + rr%4. On the last tile of a ragged range, keys
-    // past it get the raw score whose scaled value is -inf: they drop out of the maximum and
-    // their exponential is 0.
+  };
+  // sacc[kb2][rr] = raw score of query n with key tk + 8 h + koff(kb2, rr),
+  // koff = 32 kb2 + 16 (rr/8) + 4 ((rr/4)%2) + rr%4. On the last tile of a ragged range, keys
+  // past it get the raw score whose scaled value is -inf: they drop out of the maximum and their
+  // exponential is 0.
+  auto mask_tail = [&](f32x16 (&sacc)[2], int tk) __attribute__((always_inline)) {
     if (tk + kTK > t1) {
       const int rem = t1 - tk - 8 * h;
       const float excl = c_pos ? -INFINITY : INFINITY;
@@ -339,11 +327,13 @@ void attn_bf16_kernel(AttnArgs a) {
         for (int rr = 0; rr < 16; ++rr)
           if (32 * kb2 + 16 * (rr >> 3) + 4 * ((rr >> 2) & 1) + (rr & 3) >= rem) sacc[kb2][rr] = excl;
     }
-    // ---- lazily moved reference point: it moves only when a tile maximum exceeds it by more
-    // than kLazy, so the exponentials stay below 2^kLazy (exact in fp32 and bf16) and the final
-    // division by the sum of the same exponentials cancels it. Whether any query of the wave needs
-    // a move is decided from the lanes' own maxima; only then are they combined across the two
-    // lanes of a query and the accumulators rescaled.
+  };
+  // ---- lazily moved reference point: it moves only when a tile maximum exceeds it by more than
+  // kLazy, so the exponentials stay below 2^kLazy (exact in fp32 and bf16) and the final division
+  // by the sum of the same exponentials cancels it. Whether any query of the wave needs a move is
+  // decided from the lanes' own maxima; only then are they combined across the two lanes of a
+  // query and the accumulators rescaled (after the previous tile's products, before this tile's).
+  auto reference = [&](const f32x16 (&sacc)[2]) __attribute__((always_inline)) {
     float lmax;
     if (c_pos) {
       lmax = fmaxf(sacc[0][0], sacc[0][1]);
@@ -370,26 +360,69 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[hb][i] *= alpha;
     }
-    bf16x8 pf[4];  // chunk cc: keys 16 cc + 8 h + i8
-    {
-      const float mneg = -m_run;
-      float psum = 0.f;
+  };
+  // exponentials of one tile in the B-operand layout of the next product: chunk cc holds keys
+  // 16 cc + 8 h + i8
+  auto expo = [&](const f32x16 (&sacc)[2], bf16x8 (&pf)[4]) __attribute__((always_inline)) {
+    const float mneg = -m_run;
+    float psum = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
+    for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-        for (int i8 = 0; i8 < 8; ++i8) {
-          const float p = fast_exp2(fmaf(sacc[cc >> 1][8 * (cc & 1) + i8], c, mneg));
-          psum += p;
-          pf[cc][i8] = (__bf16)p;
-        }
-      l_run += psum;
+      for (int i8 = 0; i8 < 8; ++i8) {
+        const float p = fast_exp2(fmaf(sacc[cc >> 1][8 * (cc & 1) + i8], c, mneg));
+        psum += p;
+        pf[cc][i8] = (__bf16)p;
+      }
+    l_run += psum;
+  };
+  // Scores of the next tile on the matrix cores interleaved, in a fixed instruction order, with
+  // the exponentials of the current tile on the vector units: group t issues product t (block
+  // t%2, k-step t/2; its K fragment was read two groups earlier), the read for product t+2 and the
+  // exponentials of entries 2t, 2t+1 of the current tile. The scheduling barriers keep the
+  // compiler from regrouping the products and the vector work.
+  auto scores_expo = [&](const char* sK, f32x16 (&sacc)[2], const f32x16 (&cur)[2],
+                         bf16x8 (&pf)[4]) __attribute__((always_inline)) {
+    constexpr int NG = 2 * KK > 16 ? 2 * KK : 16;  // groups: products and pairs of exponentials
+    bf16x8 kf[2 * KK];
+    auto kread = [&](int t) __attribute__((always_inline)) {
+      const int key = 32 * (t & 1) + kr;
+      const int ch = (2 * (t >> 1) + h) ^ swz_k<CPR>(key);
+      kf[t] = *reinterpret_cast<const bf16x8*>(sK + key * RB + (ch << 4));
+    };
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb2][i] = 0.f;
+    kread(0);
+    kread(1);
+    const float mneg = -m_run;
+    float psum0 = 0.f, psum1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < NG; ++t) {
+      if (t < 2 * KK)
+        sacc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[t >> 1], sacc[t & 1], 0, 0, 0);
+      if (t + 2 < 2 * KK) kread(t + 2);
+      if (t < 16) {
+        const int v = 2 * t, kb2 = v >> 4, rr = v & 15;
+        const float p0 = fast_exp2(fmaf(cur[kb2][rr], c, mneg));
+        const float p1 = fast_exp2(fmaf(cur[kb2][rr + 1], c, mneg));
+        psum0 += p0;
+        psum1 += p1;
+        pf[2 * kb2 + (rr >> 3)][rr & 7] = (__bf16)p0;
+        pf[2 * kb2 + (rr >> 3)][(rr & 7) + 1] = (__bf16)p1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- O^T += V^T P^T, 16 keys per product
+    l_run += psum0 + psum1;
+  };
+  // ---- O^T += V^T P^T for the tile in ring slot `slot`, 16 keys per product
+  auto pv = [&](int slot, const bf16x8 (&pf)[4]) __attribute__((always_inline)) {
     const uint32_t vslot = ring_lds + slot * SLOT;
     uint32_t addr[NB];
 #pragma unroll
     for (int hb = 0; hb < NB; ++hb) addr[hb] = vslot + voff[hb];
-    auto pv = [&](auto cc_c) {
+    auto block = [&](auto cc_c) __attribute__((always_inline)) {
       constexpr int cc = decltype(cc_c)::value;
       s16x4 lo[NB], hi[NB];
       VtFrag<HD>::template read<cc>(addr, lo, hi);
@@ -402,11 +435,43 @@ void attn_bf16_kernel(AttnArgs a) {
                                                             oacc[hb], 0, 0, 0);
       }
     };
-    pv(std::integral_constant<int, 0>{});
-    pv(std::integral_constant<int, 1>{});
-    pv(std::integral_constant<int, 2>{});
-    pv(std::integral_constant<int, 3>{});
+    block(std::integral_constant<int, 0>{});
+    block(std::integral_constant<int, 1>{});
+    block(std::integral_constant<int, 2>{});
+    block(std::integral_constant<int, 3>{});
+  };
+
+  // Software pipeline over the 4-slot ring: while the exponentials of tile it are computed on the
+  // vector units, the matrix cores already form the scores of tile it+1; then tile it's products
+  // with V. Tile t is loaded 3 tiles ahead into the slot that tile t-4 used.
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < ntile) issue(s, ring + s * SLOT);
+  if (ntile > 2) attn_wait_vm<2 * PER>();  // tile 0 landed
+  else if (ntile > 1) attn_wait_vm<PER>();
+  else attn_wait_vm<0>();
+  asm volatile("s_barrier" ::: "memory");
+  f32x16 sa[2], sb[2];
+  scores(ring, sa);
+  mask_tail(sa, t0);
+  bf16x8 pf[4];
+
+  for (int it = 0; it + 1 < ntile; ++it) {
+    // tile it+1 landed (the only later tile in flight is it+2); every wave finished tile it-1
+    if (it + 2 < ntile) attn_wait_vm<PER>();
+    else attn_wait_vm<0>();
+    asm volatile("s_barrier" ::: "memory");
+    if (it + 3 < ntile) issue(it + 3, ring + ((it + 3) % ST) * SLOT);
+    reference(sa);
+    scores_expo(ring + ((it + 1) % ST) * SLOT, sb, sa, pf);
+    pv(it % ST, pf);
+    mask_tail(sb, t0 + (it + 1) * kTK);
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) sa[kb2] = sb[kb2];
   }
+  reference(sa);
+  expo(sa, pf);
+  pv((ntile - 1) % ST, pf);
 
   // oacc[hb][rr] = unnormalised o[query n][hd 32 hb + 8 (rr/4) + 4 h + rr%4]
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -516,9 +581,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgsF32 a) {
 static inline int cdiv(long x, long y) { return (int)((x + y - 1) / y); }
 
 // bf16 launch plan: waves per workgroup (32 query rows each) and the key split. Eight waves
-// (256 rows, one workgroup per CU, 4-deep ring) when a (sequence, kv head) has more than 160 query
-// rows on average, else four (128 rows, two workgroups per CU). The key range is split until the
-// workgroups fill every CU slot, keeping at least 128 keys per split.
+// (256 rows; at hd 128 one workgroup per CU with a 4-slot ring of 128 KB); at hd 64 four waves
+// (two workgroups per CU) when a (sequence, kv head) has at most 160 query rows on average. The
+// key range is split until the workgroups fill every CU slot, keeping at least 128 keys per split.
 struct AttnCfg {
   int nw, st, nsplit, kps;
 };
@@ -526,12 +591,12 @@ static AttnCfg plan_bf16(const ProjShape& s) {
   AttnCfg c;
   const int G = s.H / s.Hkv;
   const long rows_avg = (long)cdiv((long)s.m_cap * G, s.B);
-  c.nw = rows_avg > 160 ? 8 : 4;
+  c.nw = (s.hd == 128 || rows_avg > 160) ? 8 : 4;
 #ifdef DLLM_ATTN_FORCE_NW
   c.nw = DLLM_ATTN_FORCE_NW;
 #endif
-  c.st = (c.nw == 8 || s.hd == 64) ? 4 : 2;
-  const long slots = 256L * (c.nw == 8 ? 1 : 2);
+  c.st = 4;
+  const long slots = 256L * ((c.nw == 8 && s.hd == 128) ? 1 : 2);
   const long est = (long)s.B * s.Hkv * (rows_avg > 0 ? cdiv(rows_avg, 32 * c.nw) : 1);
   c.nsplit = 1;
   while (est * c.nsplit < slots && s.S / (c.nsplit * 2) >= 128) c.nsplit *= 2;
@@ -554,11 +619,13 @@ size_t attn_workspace_bytes(bool bf16, const ProjShape& s) {
 
 template <int HD>
 static void launch_bf16(const AttnCfg& c, dim3 grid, const AttnArgs& a, hipStream_t st) {
-  constexpr int ST4 = HD == 64 ? 4 : 2;  // ring depth of the four-wave variant (two per CU)
-  if (c.nw == 8)
-    hipLaunchKernelGGL((attn_bf16_kernel<HD, 8, 4>), grid, dim3(512), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<HD, 4, ST4>), grid, dim3(256), 0, st, a);
+  if constexpr (HD == 64) {
+    if (c.nw == 4) {
+      hipLaunchKernelGGL((attn_bf16_kernel<HD, 4, 4>), grid, dim3(256), 0, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((attn_bf16_kernel<HD, 8, 4>), grid, dim3(512), 0, st, a);
 }
 
 hipError_t launch_attn(bool bf16, const ProjShape& s, float scale, const void* q_sel,
