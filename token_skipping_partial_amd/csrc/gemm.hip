@@ -128,7 +128,7 @@ struct EpiSwiGLU {  // z[j, n] = silu(gate) * up
                                              const float u[4]) const {
     float o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = __fdividef(g[i], 1.0f + __expf(-g[i])) * u[i];
+    for (int i = 0; i < 4; ++i) o[i] = g[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[i])) * u[i];
     Elem<T>::store4(r + n, o);
   }
 };
@@ -190,14 +190,14 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const Tin* in, const 
 constexpr int kBK = 64;
 
 // Tiles of the 32 x 32 x 16 kernel used when more than 128 rows are selected (measured on MI355X
-// at the LLaDA-8B shapes): 256 x 256 tiles with 32-wide K slots for many rows (8192), 256 x 128
-// tiles with 64-wide slots for a few thousand (1640), where the larger tile count balances better.
-// Both run 8 waves as 4 x 2 (wave tiles 64 x 128 and 64 x 64).
+// at the LLaDA-8B shapes): 256 x 256 tiles for many rows (8192), 128 x 256 for a few thousand
+// (1640), where the larger tile count balances better. Both use 32-wide K slots in a 4-slot ring
+// and 8 waves (wave tiles 64 x 128 as 4 x 2, and 64 x 64 as 2 x 4).
 struct G32Shape {
   int bm, bn, bk, wm, wn, st;
 };
 constexpr G32Shape kG32Big{256, 256, 32, 4, 2, 4};
-constexpr G32Shape kG32Mid{256, 128, 64, 4, 2, 3};
+constexpr G32Shape kG32Mid{128, 256, 32, 2, 4, 4};
 constexpr int kG32BigRows = 4096;  // selected rows from which the big tile is used
 
 // ring slots that fit in the 160 KB of LDS a workgroup may use, capped at `want`
@@ -210,6 +210,7 @@ struct GemmArgs {
   const uint16_t* W;   // [N, K]  (SwiGLU: gate)
   const uint16_t* W2;  // SwiGLU: up [N, K]; else unused
   int N, K, kchunk;
+  int group;           // M-tiles walked together by the 32x32 kernel's tile order
   const int32_t* row_ptr;
   int B, m_cap;
   float* partial;      // [splits, m_cap, N] when split, else NULL
@@ -471,9 +472,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_bf16_kernel(GemmArgs g, E
   __shared__ __attribute__((aligned(1024))) char ring[ST * SLOT];
 
   const int M = live_rows(g.row_ptr, g.B, g.m_cap);
-  const int m0 = blockIdx.y * BM;
+  // Tile order: workgroups are dispatched to the 8 XCDs round-robin by linear id, so ids
+  // x, x+8, x+16, ... share one L2. They are given one contiguous run of the tile sequence, which
+  // walks g.group M-tiles at a time across all N-tiles: the tiles resident on an XCD together then
+  // share few X and W panels.
+  int mt = blockIdx.y, nt = blockIdx.x;
+  {
+    const int NT = gridDim.x, MT = gridDim.y, T = NT * MT;
+    const int lin = blockIdx.x + blockIdx.y * NT;
+    const int tt = (T % 8 == 0) ? (lin % 8) * (T / 8) + lin / 8 : lin;
+    const int gm = g.group * NT;
+    const int first = (tt / gm) * g.group;
+    const int gsize = min(MT - first, g.group);
+    mt = first + (tt % gm) % gsize;
+    nt = (tt % gm) / gsize;
+  }
+  const int m0 = mt * BM;
   if (m0 >= M) return;
-  const int n0 = blockIdx.x * (SWIGLU ? BN / 2 : BN);
+  const int n0 = nt * (SWIGLU ? BN / 2 : BN);
   const int kb = blockIdx.z * g.kchunk;
   const int nk = (min(g.K, kb + g.kchunk) - kb) / BK;  // >= 1 by the plan
 
@@ -490,31 +506,63 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_bf16_kernel(GemmArgs g, E
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // Two register buffers of fragments: A holds the first k-step of slot kt (read at the end of
+  // the previous slot), B the remaining ones. The barrier that lets slot kt+1 be read and slot kt-1
+  // be refilled sits between the first k-step's products and the rest, so the products of the
+  // first k-step cover the barrier and the latency of the next reads.
+  constexpr int KS = BK / 16;  // k-steps per slot
+  bf16x8 xa[MB], wa[NB];
+  auto read_frags = [&](const char* slot, int kk, bf16x8 (&xf)[MB], bf16x8 (&wf)[NB])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) xf[i] = frag32<BK>(slot, wm * WTM + 32 * i + l32, 2 * kk + h);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      wf[j] = frag32<BK>(slot, BM + wrow32<BN, WN, NB, SWIGLU>(wn, j) + l32, 2 * kk + h);
+  };
+  auto products = [&](const bf16x8 (&xf)[MB], const bf16x8 (&wf)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+  };
+
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
     if (s < nk)
       issue_stage32<BM, BN, BK, NW, SWIGLU>(g, ring + s * SLOT, m0, n0, M, kb + s * BK, wave, lane);
+  wait_batches<NMIN, ST - 2>(nk - 1);  // slot 0 landed (slots issued after it: min(ST-2, nk-1))
+  wg_barrier();
+  read_frags(ring, 0, xa, wa);
 
   for (int kt = 0; kt < nk; ++kt) {
-    wait_batches<NMIN, ST - 2>(nk - 1 - kt);  // slots issued after slot kt: min(ST-2, nk-1-kt)
-    wg_barrier();
-    if (kt + ST - 1 < nk)
-      issue_stage32<BM, BN, BK, NW, SWIGLU>(g, ring + ((kt + ST - 1) % ST) * SLOT, m0, n0, M,
-                                            kb + (kt + ST - 1) * BK, wave, lane);
     const char* slot = ring + (kt % ST) * SLOT;
+    bf16x8 xb[MB], wb[NB];
+    read_frags(slot, 1, xb, wb);
+    products(xa, wa);
+    if (kt + 1 < nk) {
+      // slot kt+1 landed (slots issued after it: min(ST-3, nk-2-kt) + this iteration's none yet)
+      wait_batches<NMIN, ST - 3>(nk - 2 - kt);
+      wg_barrier();  // every wave finished reading slot kt-1
+      if (kt + ST - 1 < nk)
+        issue_stage32<BM, BN, BK, NW, SWIGLU>(g, ring + ((kt + ST - 1) % ST) * SLOT, m0, n0, M,
+                                              kb + (kt + ST - 1) * BK, wave, lane);
+    }
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 xf[MB], wf[NB];
+    for (int kk = 1; kk < KS; ++kk) {
+      if (kk + 1 < KS) {
+        bf16x8 xc[MB], wc[NB];
+        read_frags(slot, kk + 1, xc, wc);
+        products(xb, wb);
 #pragma unroll
-      for (int i = 0; i < MB; ++i) xf[i] = frag32<BK>(slot, wm * WTM + 32 * i + l32, 2 * kk + h);
+        for (int i = 0; i < MB; ++i) xb[i] = xc[i];
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        wf[j] = frag32<BK>(slot, BM + wrow32<BN, WN, NB, SWIGLU>(wn, j) + l32, 2 * kk + h);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NB; ++j) wb[j] = wc[j];
+      } else {
+        if (kt + 1 < nk) read_frags(ring + ((kt + 1) % ST) * SLOT, 0, xa, wa);
+        products(xb, wb);
+      }
     }
   }
 
@@ -779,6 +827,9 @@ static hipError_t run_gemm_bf16(const GemmPlan& p, const uint16_t* X, const uint
   GemmArgs g;
   g.X = X; g.W = W; g.W2 = W2; g.N = N; g.K = K;
   g.kchunk = kchunk_of(p, K);
+  // measured at the LLaDA shapes: all row tiles together up to 8 of them, else 4
+  const int mtiles = cdiv(m_cap, p.bm);
+  g.group = mtiles <= 8 ? mtiles : 4;
   g.row_ptr = row_ptr; g.B = B; g.m_cap = m_cap;
   g.partial = (p.splits > 1) ? partial : nullptr;
   const int cols = SWIGLU ? p.bn / 2 : p.bn;
