@@ -19,6 +19,11 @@ It computes, slowly and in float64, what the five library calls compute:
                       recomputed exactly; §1: attention is bidirectional (no causal mask).
   gather_ffn_scatter  DyLLM (French page) §2.A: FFN runs for salient tokens only, the others
                       reuse cached activations.
+  salient_attention   DyLLM (French page) §2.B, both paths: exact rows for salient tokens; for
+                      stable tokens the weights of unchanged keys are reused and only the changed
+                      keys' contributions are replaced, which equals attention of the reused query
+                      against the updated cache (see the function); gather_kv_rows copies the K/V
+                      rows that a step is about to overwrite.
 
 Readings where the pages are silent (all listed in the design notes): confidence c is the maximum
 softmax probability of the previous-step logits at temperature 1; the transformer block is
@@ -216,6 +221,73 @@ def partial_attn(q_sel, k_cache, v_cache, sel_idx, row_ptr, H: int, Hkv: int, hd
             p /= np.sum(p, axis=1, keepdims=True)
             out[rows, h, :] = p @ v_cache[b, hk]
     return out.reshape(M, H * hd)
+
+
+# ----------------------------------------------------------------------------------------------
+# attention context of every token: exact rows for the salient tokens, reused rows for the rest
+# ----------------------------------------------------------------------------------------------
+def gather_kv_rows(k_cache, v_cache, sel_idx, row_ptr):
+    """Copies of the K/V cache rows at the selected positions, taken before a projection call
+    overwrites them: k_rows[r] = k_cache[b, :, s, :] for selected token r = (b, s).
+
+    Returns (k_rows [M, Hkv, hd], v_rows [M, Hkv, hd]).
+    """
+    k_cache = np.asarray(k_cache)
+    v_cache = np.asarray(v_cache)
+    S = k_cache.shape[2]
+    M = int(row_ptr[-1])
+    ids = np.asarray(sel_idx[:M], dtype=np.int64)
+    return k_cache[ids // S, :, ids % S, :].copy(), v_cache[ids // S, :, ids % S, :].copy()
+
+
+def context_all(q_all, k_cache, v_cache, H: int, Hkv: int, hd: int, scale: float):
+    """Attention context of every token's query against every cached key (no mask).
+
+    o[b, s, h] = softmax_t(scale * q[b, s, h] . k[b, hk, t]) . v[b, hk, t], hk = h // (H / Hkv),
+    and lse[b, s, h] = ln sum_t exp(scale * q[b, s, h] . k[b, hk, t]).
+    Returns (o [B, S, H*hd], lse [B, S, H]).
+    """
+    q = np.asarray(q_all, dtype=np.float64)
+    k_cache = np.asarray(k_cache, dtype=np.float64)
+    v_cache = np.asarray(v_cache, dtype=np.float64)
+    B, _, S, _ = k_cache.shape
+    G = H // Hkv
+    q = q.reshape(B, S, H, hd)
+    o = np.zeros((B, S, H, hd))
+    lse = np.zeros((B, S, H))
+    for b in range(B):
+        for h in range(H):
+            s = (q[b, :, h, :] @ k_cache[b, h // G].T) * scale              # [S queries, S keys]
+            mx = np.max(s, axis=1, keepdims=True)
+            e = np.exp(s - mx)
+            tot = np.sum(e, axis=1, keepdims=True)
+            o[b, :, h, :] = (e / tot) @ v_cache[b, h // G]
+            lse[b, :, h] = (mx + np.log(tot))[:, 0]
+    return o.reshape(B, S, H * hd), lse
+
+
+def salient_attention(q_sel, q_all, k_cache, v_cache, sel_idx, row_ptr, H: int, Hkv: int,
+                      hd: int, scale: float):
+    """DyLLM (French page) §2.B, both paths of one step, given the caches after the projection
+    call of the step overwrote the K/V rows of the selected tokens:
+      salient tokens (selected): their query is the one just projected and their attention row
+        is recomputed exactly against every cached key;
+      stable tokens (the rest): their query from the step that last projected them is reused,
+        and their context takes in the changed K/V rows. Reusing the previous step's weights of
+        the unchanged keys and replacing only the changed keys' contributions gives, exactly, the
+        attention of the reused query against the updated cache.
+    So the context of every token is the attention of the query cache, with the selected rows
+    replaced, against the updated K/V cache.
+
+    Returns (q_all' [B, S, H*hd], o [B, S, H*hd], lse [B, S, H]).
+    """
+    q_new = np.array(q_all, dtype=np.float64, copy=True)
+    B, S = q_new.shape[:2]
+    M = int(row_ptr[-1])
+    ids = np.asarray(sel_idx[:M], dtype=np.int64)
+    q_new[ids // S, ids % S] = np.asarray(q_sel, dtype=np.float64)[:M]
+    o, lse = context_all(q_new, k_cache, v_cache, H, Hkv, hd, scale)
+    return q_new, o, lse
 
 
 # ----------------------------------------------------------------------------------------------

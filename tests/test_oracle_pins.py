@@ -266,6 +266,116 @@ def test_attention_grouped_heads_are_blocked():
     assert np.allclose(o[2], [-1, 2]) and np.allclose(o[3], [-1, 2])
 
 
+# --------------------------------------------------- context of every token (DyLLM §2.B paths)
+def test_context_all_brute_force_python_loops():
+    B, S, H, Hkv, hd = 2, 4, 4, 2, 3
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((B, S, H * hd))
+    kc = rng.standard_normal((B, Hkv, S, hd))
+    vc = rng.standard_normal((B, Hkv, S, hd))
+    scale = 0.61
+    o, lse = O.context_all(q, kc, vc, H, Hkv, hd, scale)
+    G = H // Hkv
+    for b in range(B):
+        for s_ in range(S):
+            for h in range(H):
+                hk = h // G
+                logit = [scale * sum(q[b, s_, h * hd + e] * kc[b, hk, t, e] for e in range(hd))
+                         for t in range(S)]
+                w = [math.exp(x) for x in logit]
+                tot = sum(w)
+                assert lse[b, s_, h] == pytest.approx(math.log(tot), rel=1e-12, abs=1e-13)
+                for e in range(hd):
+                    want = sum(w[t] * vc[b, hk, t, e] for t in range(S)) / tot
+                    assert o[b, s_, h * hd + e] == pytest.approx(want, rel=1e-12, abs=1e-14)
+
+
+def test_context_all_special_cases():
+    B, S, H, Hkv, hd = 1, 5, 2, 1, 4
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((B, S, H * hd))
+    kc = rng.standard_normal((B, Hkv, S, hd))
+    vc = rng.standard_normal((B, Hkv, S, hd))
+    # identical keys: uniform weights, lse = scale q.k + ln S
+    same_k = np.broadcast_to(kc[:, :, :1], kc.shape).copy()
+    o, lse = O.context_all(q, same_k, vc, H, Hkv, hd, 0.5)
+    assert np.allclose(o.reshape(S, H, hd), vc[0, 0].mean(axis=0), rtol=1e-13)
+    qk = q.reshape(S, H, hd) @ kc[0, 0, 0]
+    assert np.allclose(lse[0], 0.5 * qk + math.log(S), rtol=1e-13)
+    # one key: o = v0, lse = scale q.k0
+    o, lse = O.context_all(q[:, :1], kc[:, :, :1], vc[:, :, :1], H, Hkv, hd, 0.5)
+    assert np.allclose(o.reshape(H, hd), vc[0, 0, 0], rtol=1e-14)
+    assert np.allclose(lse[0, 0], 0.5 * (q[0, 0].reshape(H, hd) @ kc[0, 0, 0]), rtol=1e-14)
+
+
+def test_gather_kv_rows_copies_the_selected_positions():
+    B, Hkv, S, hd = 2, 3, 5, 2
+    kc = np.arange(B * Hkv * S * hd, dtype=np.float64).reshape(B, Hkv, S, hd)
+    vc = -kc
+    sel = np.array([1, 4, 7], np.int32)   # (0,1), (0,4), (1,2)
+    rp = np.array([0, 2, 3], np.int32)
+    kr, vr = O.gather_kv_rows(kc, vc, sel, rp)
+    for r, (b, s_) in enumerate([(0, 1), (0, 4), (1, 2)]):
+        for hk in range(Hkv):
+            assert list(kr[r, hk]) == list(kc[b, hk, s_])
+            assert list(vr[r, hk]) == list(vc[b, hk, s_])
+
+
+def test_salient_attention_rows_use_the_right_query():
+    """Selected rows attend with the new query, the rest with the cached one (compared with the
+    separately written partial_attn, itself pinned by brute force above)."""
+    B, S, H, Hkv, hd = 2, 6, 4, 2, 3
+    rng = np.random.default_rng(7)
+    q_all = rng.standard_normal((B, S, H * hd))
+    kc = rng.standard_normal((B, Hkv, S, hd))
+    vc = rng.standard_normal((B, Hkv, S, hd))
+    sel = np.array([2, 3, 7], np.int32)
+    rp = np.array([0, 2, 3], np.int32)
+    q_sel = rng.standard_normal((3, H * hd))
+    q_new, o, _ = O.salient_attention(q_sel, q_all, kc, vc, sel, rp, H, Hkv, hd, 0.4)
+    want_sel = O.partial_attn(q_sel, kc, vc, sel, rp, H, Hkv, hd, 0.4)
+    for r, flat in enumerate(sel):
+        assert np.allclose(o[flat // S, flat % S], want_sel[r], rtol=1e-13)
+        assert np.array_equal(q_new[flat // S, flat % S], q_sel[r])
+    rest = np.array([i for i in range(B * S) if i not in set(sel.tolist())], np.int32)
+    rp_rest = np.array([0, int(np.sum(rest < S)), len(rest)], np.int32)
+    q_rest = q_all.reshape(B * S, -1)[rest]
+    want_rest = O.partial_attn(q_rest, kc, vc, rest, rp_rest, H, Hkv, hd, 0.4)
+    for r, flat in enumerate(rest):
+        assert np.allclose(o[flat // S, flat % S], want_rest[r], rtol=1e-13)
+        assert np.array_equal(q_new[flat // S, flat % S], q_all[flat // S, flat % S])
+
+
+def test_stable_rows_equal_reused_weights_plus_changed_contributions():
+    """DyLLM §2.B, non-salient path, done incrementally in this test: keep the previous step's
+    softmax numerator and denominator of a stable token, take out the old rows of the changed
+    keys, put in the new ones. The result must be the oracle's context of the reused query
+    against the updated cache."""
+    S, hd, scale = 7, 4, 0.45
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, S, hd))
+    k_old = rng.standard_normal((1, 1, S, hd))
+    v_old = rng.standard_normal((1, 1, S, hd))
+    changed = [1, 4, 5]
+    k_new, v_new = k_old.copy(), v_old.copy()
+    k_new[0, 0, changed] = rng.standard_normal((3, hd))
+    v_new[0, 0, changed] = rng.standard_normal((3, hd))
+    o_new, lse_new = O.context_all(q, k_new, v_new, 1, 1, hd, scale)
+    for i in range(S):
+        w = [math.exp(scale * float(q[0, i] @ k_old[0, 0, t])) for t in range(S)]
+        den = sum(w)
+        num = [sum(w[t] * v_old[0, 0, t, e] for t in range(S)) for e in range(hd)]
+        for t in changed:
+            w_old = math.exp(scale * float(q[0, i] @ k_old[0, 0, t]))
+            w_new = math.exp(scale * float(q[0, i] @ k_new[0, 0, t]))
+            den += w_new - w_old
+            for e in range(hd):
+                num[e] += w_new * v_new[0, 0, t, e] - w_old * v_old[0, 0, t, e]
+        assert lse_new[0, i, 0] == pytest.approx(math.log(den), rel=1e-12)
+        for e in range(hd):
+            assert o_new[0, i, e] == pytest.approx(num[e] / den, rel=1e-11, abs=1e-13)
+
+
 # ------------------------------------------------------------------------------ FFN
 def test_ffn_zero_projections_copy_rows_exactly():
     B, S, d, F = 2, 4, 8, 16
