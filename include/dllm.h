@@ -11,6 +11,11 @@
  *   dllm_gather_ffn_scatter     output projection + SwiGLU FFN of the selected tokens, scattered
  *                               back into the cached hidden states
  *
+ * and, for a step that keeps the attention context of every token (not only the selected ones):
+ *
+ *   dllm_gather_kv_rows         copies of the K/V rows a projection call is about to overwrite
+ *   dllm_salient_attn           exact rows for the selected tokens, changed-key update for the rest
+ *
  * Sources (web pages; section names as printed there):
  *   [ES-dLLM]  "ES-dLLM: Efficient Inference for Diffusion Large Language Models by Early-Skipping",
  *              German summary page §2.A (importance-score equation, alpha = 0.5) and §2.B (top-k
@@ -84,6 +89,7 @@ typedef struct {
 } dllm_shape;
 
 #define DLLM_MAX_SELECT_S 8192 /* largest S dllm_select_compact accepts (one row lives in LDS) */
+#define DLLM_MAX_SALIENT_S 8192 /* largest S dllm_salient_attn accepts (changed list in LDS) */
 
 /* (1) Saliency [ES-dLLM §2.A equation; DyLLM §2.A].
  *   score[b,s] = alpha * c[b,s] + (1 - alpha) * delta[b,s]
@@ -160,6 +166,48 @@ dllm_status dllm_gather_ffn_scatter(const dllm_shape* shape,
                                     const void* w_down, const int32_t* sel_idx,
                                     const int32_t* row_ptr, int32_t m_cap, void* h_out,
                                     void* ws, size_t ws_bytes, void* stream);
+
+/* Copies of the K/V rows at the selected positions [DyLLM §2.B: the stable-token update takes
+ * out the contributions of the changed keys' previous rows, so those rows are copied before
+ * dllm_gather_qkv_scatter_kv overwrites them].
+ * For j < M = min(row_ptr[B], m_cap), with (b, s) = (sel_idx[j] / S, sel_idx[j] % S):
+ *   k_rows[j, hk, :] = k_cache[b, hk, s, :];  v_rows[j, hk, :] = v_cache[b, hk, s, :]
+ * k_cache, v_cache : [B, Hkv, S, hd] dtype;  k_rows, v_rows : [m_cap, Hkv, hd] dtype.
+ * Bit-exact copies. hd in {64,128}. Workspace: none. */
+dllm_status dllm_gather_kv_rows(const dllm_shape* shape, const void* k_cache, const void* v_cache,
+                                const int32_t* sel_idx, const int32_t* row_ptr, int32_t m_cap,
+                                void* k_rows, void* v_rows, void* stream);
+
+/* Attention context of every token [DyLLM §2.B: exact rows for salient tokens; for stable
+ * tokens the previous step's weights of the unchanged keys are reused and only the contributions
+ * of the changed keys are replaced, so the cost is O(S |selected|) instead of O(S^2)].
+ * Per-token softmax state, kept by the caller from step to step (positions p = b*S + s):
+ *   st_m[p, h]  reference point in base-2 units of the scaled scores,
+ *   st_l[p, h]  sum over every key t of 2^(scale log2(e) q.k_t - st_m),
+ *   st_o[p, h*hd : (h+1)*hd]  the normalised context (float32);
+ *   so ln sum_t exp(scale q.k_t) = ln(2) (st_m + log2 st_l), and q_all[p] is the query the state
+ *   belongs to.
+ * Given caches already holding this step's K/V rows at the selected positions (after
+ * dllm_gather_qkv_scatter_kv) and k_old, v_old from dllm_gather_kv_rows taken before it:
+ *   selected token j:  q_all[p] = q_sel[j]; its state and context are recomputed exactly against
+ *                      every key (as dllm_partial_attn); o_sel[j] as dllm_partial_attn writes it;
+ *   any other token:   its state is updated with the old rows of the changed keys taken out and
+ *                      the new rows put in, against its stored query q_all[p];
+ *   o_all[p] = st_o[p] rounded to dtype, for every position.
+ * The result for every token is the attention of q_all (after the update) against the updated
+ * cache, up to rounding, provided the state held that attention for the previous cache.
+ * Initialise the state with a call that selects every position (then nothing is "other").
+ * q_sel : [m_cap, H hd]; q_all : [B, S, H hd] (updated in place); k_cache, v_cache :
+ * [B, Hkv, S, hd]; k_old, v_old : [m_cap, Hkv, hd]; st_m, st_l : [B, S, H] float32; st_o :
+ * [B, S, H hd] float32 (updated in place); o_sel : [m_cap, H hd]; o_all : [B, S, H hd].
+ * bf16 only (DLLM_ERR_UNSUPPORTED for float32); S <= DLLM_MAX_SALIENT_S; hd in {64,128}; scale
+ * finite. Workspace: dllm_workspace_bytes(DLLM_OP_ATTN, shape, m_cap). */
+dllm_status dllm_salient_attn(const dllm_shape* shape, float scale, const void* q_sel,
+                              void* q_all, const void* k_cache, const void* v_cache,
+                              const void* k_old, const void* v_old, const int32_t* sel_idx,
+                              const int32_t* row_ptr, int32_t m_cap, float* st_m, float* st_l,
+                              float* st_o, void* o_sel, void* o_all, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /* Bytes of device workspace the call `op` (a dllm_op) needs for this shape and m_cap; 0 when
  * none. Returns (size_t)-1 for an invalid op or shape. Pure host function. */

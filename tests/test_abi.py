@@ -143,3 +143,29 @@ def test_layer_call_validation():
     assert need > 0  # batch 1, M = 128 splits the key range
     st = lib.dllm_partial_attn(ctypes.byref(s), 0.1, P, P, P, P, P, 128, P, P, need - 1, None)
     assert st == tsp.DLLM_ERR_WORKSPACE
+
+
+def test_context_call_validation():
+    s = llada()
+    g, c = tsp.dllm_gather_kv_rows, tsp.dllm_salient_attn
+    ws = None
+    assert rc(g, s, None, P, P, P, 128, P, P) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(g, s, P, P, P, P, 1025, P, P) == tsp.DLLM_ERR_INVALID_ARG      # m_cap > B*S
+    assert rc(g, s, P, P, P, P, 128, P + 4, P) == tsp.DLLM_ERR_INVALID_ARG   # misaligned
+    bad = llada(); bad.hd = 96
+    assert rc(g, bad, P, P, P, P, 128, P, P) == tsp.DLLM_ERR_UNSUPPORTED
+    full = (P,) * 6  # q_sel, q_all, k_cache, v_cache, k_old, v_old
+    assert rc(c, s, 0.1, *full, None, P, 128, P, P, P, P, P, ws) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(c, s, 0.1, *full, P, P, 128, P, None, P, P, P, ws) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(c, s, float("nan"), *full, P, P, 128, P, P, P, P, P, ws) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(c, s, 0.1, P, P + 2, *(P,) * 4, P, P, 128, P, P, P, P, P, ws) == \
+        tsp.DLLM_ERR_INVALID_ARG
+    f32 = llada(dtype="f32")
+    assert rc(c, f32, 0.1, *full, P, P, 128, P, P, P, P, P, ws) == tsp.DLLM_ERR_UNSUPPORTED
+    long = llada(S=tsp.MAX_SALIENT_S + 8)
+    assert rc(c, long, 0.1, *full, P, P, 128, P, P, P, P, P, ws) == tsp.DLLM_ERR_UNSUPPORTED
+    lib = tsp.library()
+    need = tsp.dllm_workspace_bytes(tsp.OP_ATTN, s, 128)
+    st = lib.dllm_salient_attn(ctypes.byref(s), 0.1, P, P, P, P, P, P, P, P, 128, P, P, P, P, P,
+                               P, need - 1, None)
+    assert st == tsp.DLLM_ERR_WORKSPACE

@@ -24,10 +24,11 @@ DELTA_L1N, DELTA_COS, DELTA_L2R = 0, 1, 2
 SEL_THRESHOLD, SEL_TOPK = 0, 1
 OP_SALIENCY, OP_SELECT, OP_QKV, OP_ATTN, OP_FFN = range(5)
 MAX_SELECT_S = 8192
+MAX_SALIENT_S = 8192
 
 EXPORTS = ("dllm_saliency", "dllm_select_compact", "dllm_gather_qkv_scatter_kv",
-           "dllm_partial_attn", "dllm_gather_ffn_scatter", "dllm_workspace_bytes",
-           "dllm_status_string", "dllm_version")
+           "dllm_partial_attn", "dllm_gather_ffn_scatter", "dllm_gather_kv_rows",
+           "dllm_salient_attn", "dllm_workspace_bytes", "dllm_status_string", "dllm_version")
 
 
 class DllmError(RuntimeError):
@@ -71,6 +72,8 @@ def _load():
         "dllm_gather_qkv_scatter_kv": (I32, [SP, P, P, P, P, P, I32, P, P, P, P, SZ, P]),
         "dllm_partial_attn": (I32, [SP, F, P, P, P, P, P, I32, P, P, SZ, P]),
         "dllm_gather_ffn_scatter": (I32, [SP, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]),
+        "dllm_gather_kv_rows": (I32, [SP, P, P, P, P, I32, P, P, P]),
+        "dllm_salient_attn": (I32, [SP, F, P, P, P, P, P, P, P, P, I32, P, P, P, P, P, P, SZ, P]),
         "dllm_workspace_bytes": (SZ, [I32, SP, I32]),
         "dllm_status_string": (ctypes.c_char_p, [I32]),
         "dllm_version": (I32, []),
@@ -175,3 +178,20 @@ def dllm_gather_ffn_scatter(shape, h_in, o_sel, w_o, g_ffn, w_gate, w_up, w_down
                                         _ptr(g_ffn), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                         _ptr(sel_idx), _ptr(row_ptr), int(m_cap), _ptr(h_out),
                                         wp, wn, _stream(stream)), "dllm_gather_ffn_scatter")
+
+
+def dllm_gather_kv_rows(shape, k_cache, v_cache, sel_idx, row_ptr, m_cap, k_rows, v_rows,
+                        stream=None):
+    _check(_lib.dllm_gather_kv_rows(ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(sel_idx), _ptr(row_ptr), int(m_cap), _ptr(k_rows),
+                                    _ptr(v_rows), _stream(stream)), "dllm_gather_kv_rows")
+
+
+def dllm_salient_attn(shape, scale, q_sel, q_all, k_cache, v_cache, k_old, v_old, sel_idx,
+                      row_ptr, m_cap, st_m, st_l, st_o, o_sel, o_all, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(_lib.dllm_salient_attn(ctypes.byref(shape), float(scale), _ptr(q_sel), _ptr(q_all),
+                                  _ptr(k_cache), _ptr(v_cache), _ptr(k_old), _ptr(v_old),
+                                  _ptr(sel_idx), _ptr(row_ptr), int(m_cap), _ptr(st_m),
+                                  _ptr(st_l), _ptr(st_o), _ptr(o_sel), _ptr(o_all), wp, wn,
+                                  _stream(stream)), "dllm_salient_attn")

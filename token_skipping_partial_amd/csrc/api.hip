@@ -49,7 +49,8 @@ dllm_status ws_status(const void* ws, size_t have, size_t need) {
 
 extern "C" {
 
-int32_t dllm_version(void) { return 100; }
+static_assert(DLLM_MAX_SALIENT_S == kSalientMaxS, "stable-token pass limit");
+int32_t dllm_version(void) { return 101; }
 
 const char* dllm_status_string(int32_t status) {
   switch (status) {
@@ -203,6 +204,42 @@ dllm_status dllm_gather_ffn_scatter(const dllm_shape* shape, const void* h_in, c
   if ((st = ws_status(ws, ws_bytes, ffn_workspace_bytes(bf16, p))) != DLLM_OK) return st;
   return hip_status(launch_ffn(bf16, p, h_in, o_sel, w_o, g_ffn, w_gate, w_up, w_down, sel_idx,
                                row_ptr, h_out, ws, (hipStream_t)stream));
+}
+
+dllm_status dllm_gather_kv_rows(const dllm_shape* shape, const void* k_cache, const void* v_cache,
+                                const int32_t* sel_idx, const int32_t* row_ptr, int32_t m_cap,
+                                void* k_rows, void* v_rows, void* stream) {
+  dllm_status st = layer_shape_status(shape, m_cap);
+  if (st != DLLM_OK) return st;
+  if (!k_cache || !v_cache || !sel_idx || !row_ptr || !k_rows || !v_rows)
+    return DLLM_ERR_INVALID_ARG;
+  for (const void* p : {k_cache, v_cache, (const void*)k_rows, (const void*)v_rows})
+    if (!aligned16(p)) return DLLM_ERR_INVALID_ARG;
+  const size_t elem = shape->dtype == DLLM_BF16 ? 2 : 4;
+  return hip_status(launch_gather_kv_rows(proj_shape(shape, m_cap), elem, k_cache, v_cache,
+                                          sel_idx, row_ptr, k_rows, v_rows, (hipStream_t)stream));
+}
+
+dllm_status dllm_salient_attn(const dllm_shape* shape, float scale, const void* q_sel,
+                              void* q_all, const void* k_cache, const void* v_cache,
+                              const void* k_old, const void* v_old, const int32_t* sel_idx,
+                              const int32_t* row_ptr, int32_t m_cap, float* st_m, float* st_l,
+                              float* st_o, void* o_sel, void* o_all, void* ws, size_t ws_bytes,
+                              void* stream) {
+  dllm_status st = layer_shape_status(shape, m_cap);
+  if (st != DLLM_OK) return st;
+  if (!q_sel || !q_all || !k_cache || !v_cache || !k_old || !v_old || !sel_idx || !row_ptr ||
+      !st_m || !st_l || !st_o || !o_sel || !o_all || !isfinite(scale))
+    return DLLM_ERR_INVALID_ARG;
+  for (const void* p : {q_sel, (const void*)q_all, k_cache, v_cache, k_old, v_old,
+                        (const void*)st_o, (const void*)o_sel, (const void*)o_all})
+    if (!aligned16(p)) return DLLM_ERR_INVALID_ARG;
+  if (shape->dtype != DLLM_BF16 || shape->S > DLLM_MAX_SALIENT_S) return DLLM_ERR_UNSUPPORTED;
+  const ProjShape p = proj_shape(shape, m_cap);
+  if ((st = ws_status(ws, ws_bytes, attn_workspace_bytes(true, p))) != DLLM_OK) return st;
+  return hip_status(launch_salient_attn(p, scale, q_sel, q_all, k_cache, v_cache, k_old, v_old,
+                                        sel_idx, row_ptr, st_m, st_l, st_o, o_sel, o_all, ws,
+                                        (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -41,7 +41,19 @@ struct AttnArgs {
   float* part_ml;  // [nsplit, m_cap, H, 2]
   int B, S, H, Hkv, m_cap, nsplit, kps;
   float scale_log2;  // scale * log2(e): scores are kept in base-2 units
+  // context of every token (NULL in the selected-rows-only call): per-token softmax state
+  // (reference m in base-2 units, sum l of 2^(score - m), normalised context o in fp32), the
+  // bf16 context and query of every token, and the compact copies of the overwritten K/V rows
+  const int32_t* sel_idx;
+  float* st_m;        // [B*S, H]
+  float* st_l;        // [B*S, H]
+  float* st_o;        // [B*S, H*hd]
+  uint16_t* o_all;    // [B*S, H*hd]
+  uint16_t* q_all;    // [B*S, H*hd]
+  const uint16_t* k_old;  // [m_cap, Hkv, hd]
+  const uint16_t* v_old;
 };
+constexpr int kDeltaMaxS = kSalientMaxS;  // the changed-position list of a sequence lives in LDS
 
 typedef __attribute__((address_space(3))) void lds_void_a;
 typedef short __attribute__((ext_vector_type(4))) s16x4;
@@ -186,7 +198,16 @@ struct VtFrag<64> {
 // grid.x enumerates (sequence, kv head, key split) and grid.y the query tiles, so the tiles that
 // share one K/V panel have ids grid.x apart: with grid.x a multiple of 8 they run on the same XCD
 // and read the panel through one L2.
-template <int HD, int NW, int ST>
+//
+// DELTA: the stable-token pass of DyLLM (French summary page) §2.B. The queries are every
+// position of the sequence (their cached query vectors), and the keys are the changed rows only:
+// tile t holds the new K/V rows of selected entries 32t .. 32t+31 (rows 0-31, gathered from the
+// cache) and their old rows (rows 32-63, from the copies taken before the projection call). The
+// old rows' exponentials enter with a negative sign, so the tile loop accumulates the change of
+// the softmax numerator and denominator relative to the token's stored reference point; the
+// epilogue adds it to the stored state. Rows of selected positions are computed too and are
+// overwritten by the exact pass that runs next.
+template <int HD, int NW, int ST, bool DELTA>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr int KK = HD / 16;              // 16-wide k-steps of q.k over hd
@@ -199,7 +220,8 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int PER = SLOT / 1024 / NW;    // DMA instructions per wave per tile (K half, V half)
   constexpr int TQ = 32 * NW;              // query rows per workgroup
   static_assert(PER % 2 == 0 && ST >= 2 && (ST - 2) * PER < 64, "tile shape");
-  __shared__ __attribute__((aligned(1024))) char ring[ST * SLOT];
+  // DELTA: the ring is followed by the list of changed positions of the sequence
+  __shared__ __attribute__((aligned(1024))) char ring[ST * SLOT + (DELTA ? kDeltaMaxS * 4 : 0)];
 
   const int G = a.H / a.Hkv;
   const int Nq = a.H * HD;
@@ -209,26 +231,30 @@ void attn_bf16_kernel(AttnArgs a) {
   const int split = blockIdx.x - b * per_b - hk * a.nsplit;
   const int M = min(a.row_ptr[a.B], a.m_cap);
   const int r0 = min(a.row_ptr[b], M), r1 = min(a.row_ptr[b + 1], M);
-  const int nrows = (r1 - r0) * G;
+  const int nA = r1 - r0;  // selected (changed) positions of the sequence
+  const int nrows = DELTA ? a.S * G : nA * G;
   const int tile0 = blockIdx.y * TQ;
   if (tile0 >= nrows) return;
-  const int t0 = split * a.kps;
-  const int t1 = min(a.S, t0 + a.kps);
-  const int ntile = (t1 - t0 + kTK - 1) / kTK;
+  // key range [t0, t1) of this split; DELTA: entries [0, nA) of the changed list, 32 per tile
+  const int t0 = DELTA ? 0 : split * a.kps;
+  const int t1 = DELTA ? nA : min(a.S, t0 + a.kps);
+  const int ntile = DELTA ? (nA + 31) / 32 : (t1 - t0 + kTK - 1) / kTK;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5, g = lane >> 4, q16 = lane & 15;
 
-  // ---- this lane's query: column n of the wave's 32-query block
+  // ---- this lane's query: column n of the wave's 32-query block. qj: compact row of a selected
+  // token, or (DELTA) the flat position b*S + s
   const int qr = tile0 + 32 * wave + n;
   const bool qvalid = qr < nrows;
-  const int qj = qvalid ? r0 + qr / G : 0;
+  const int qj = qvalid ? (DELTA ? b * a.S + qr / G : r0 + qr / G) : 0;
   const int qh = qvalid ? hk * G + qr % G : 0;
+  const uint16_t* qsrc = DELTA ? a.q_all : a.q;
   bf16x8 qf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
-    qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(a.q + (size_t)qj * Nq + qh * HD + 16 * kk + 8 * h)
+    qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(qsrc + (size_t)qj * Nq + qh * HD + 16 * kk + 8 * h)
                     : bf16x8{};
 
   f32x16 oacc[NB];
@@ -237,8 +263,16 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[hb][i] = 0.f;
   // m_run: reference point of the exponentials (base-2 units), the same in the two lanes of a
-  // query; l_run: this lane's share (its 32 keys of every tile) of the sum of exponentials
-  float m_run = -INFINITY, l_run = 0.f;
+  // query; l_run: this lane's share (its 32 keys of every tile) of the sum of exponentials.
+  // DELTA starts from the token's stored reference point.
+  const float m_state = (DELTA && qvalid) ? a.st_m[(size_t)qj * a.H + qh] : 0.f;
+  float m_run = DELTA ? m_state : -INFINITY, l_run = 0.f;
+  const int* apos = reinterpret_cast<const int*>(ring + ST * SLOT);
+  if constexpr (DELTA) {
+    int* wpos = reinterpret_cast<int*>(ring + ST * SLOT);
+    for (int i = tid; i < nA; i += 64 * NW) wpos[i] = a.sel_idx[r0 + i] - b * a.S;
+    __syncthreads();
+  }
 
   const size_t head_off = ((size_t)b * a.Hkv + hk) * (size_t)a.S * HD;
   const uint16_t* kbase = a.kc + head_off;
@@ -252,6 +286,22 @@ void attn_bf16_kernel(AttnArgs a) {
   const uint32_t doff_k = (uint32_t)(rw * RB + 16 * ((lane % CPR) ^ swz_k<CPR>(rw)));
   const uint32_t doff_v = (uint32_t)(rw * RB + 16 * ((lane % CPR) ^ swz_v<CPR>(rw)));
   auto issue = [&](int it, char* slot) {
+    if constexpr (DELTA) {  // rows 0-31: new rows of changed entries 32 it + r; rows 32-63: old
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const bool isk = p < PER / 2;
+        const int pp = isk ? p : p - PER / 2;
+        const int row = RPI * (wave + NW * pp) + lane / CPR;
+        const int j = min(32 * it + (row & 31), nA - 1);  // past the list: repeat its last entry
+        const int cch = (lane % CPR) ^ (isk ? swz_k<CPR>(row) : swz_v<CPR>(row));
+        const uint16_t* src = row < 32 ? (isk ? kbase : vbase) + (size_t)apos[j] * HD
+                                       : (isk ? a.k_old : a.v_old) + ((size_t)(r0 + j) * a.Hkv + hk) * HD;
+        __builtin_amdgcn_global_load_lds(src + 8 * cch,
+                                         (lds_void_a*)(slot + (isk ? 0 : HALF) + (wave + NW * pp) * 1024),
+                                         16, 0, 0);
+      }
+      return;
+    }
     const int tk = t0 + it * kTK;
     if (tk + kTK <= t1) {
 #pragma unroll
@@ -316,18 +366,23 @@ void attn_bf16_kernel(AttnArgs a) {
   // sacc[kb2][rr] = raw score of query n with key tk + 8 h + koff(kb2, rr),
   // koff = 32 kb2 + 16 (rr/8) + 4 ((rr/4)%2) + rr%4. On the last tile of a ragged range, keys
   // past it get the raw score whose scaled value is -inf: they drop out of the maximum and their
-  // exponential is 0.
-  auto mask_tail = [&](f32x16 (&sacc)[2], int tk) __attribute__((always_inline)) {
-    if (tk + kTK > t1) {
+  // exponential is 0. DELTA: both halves (new and old rows) hold entries 32 it + 8 h + koff % 32.
+  auto mask_tail = [&](f32x16 (&sacc)[2], int it) __attribute__((always_inline)) {
+    const int span = DELTA ? 32 : kTK;
+    const int tk = t0 + it * span;
+    if (tk + span > t1) {
       const int rem = t1 - tk - 8 * h;
       const float excl = c_pos ? -INFINITY : INFINITY;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
-          if (32 * kb2 + 16 * (rr >> 3) + 4 * ((rr >> 2) & 1) + (rr & 3) >= rem) sacc[kb2][rr] = excl;
+          if ((DELTA ? 0 : 32 * kb2) + 16 * (rr >> 3) + 4 * ((rr >> 2) & 1) + (rr & 3) >= rem)
+            sacc[kb2][rr] = excl;
     }
   };
+  // DELTA: the old rows (block 1, chunks 2 and 3) enter with a negative sign
+  auto sgn = [](int kb2) constexpr { return (DELTA && kb2 == 1) ? -1.f : 1.f; };
   // ---- lazily moved reference point: it moves only when a tile maximum exceeds it by more than
   // kLazy, so the exponentials stay below 2^kLazy (exact in fp32 and bf16) and the final division
   // by the sum of the same exponentials cancels it. Whether any query of the wave needs a move is
@@ -370,7 +425,7 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
       for (int i8 = 0; i8 < 8; ++i8) {
-        const float p = fast_exp2(fmaf(sacc[cc >> 1][8 * (cc & 1) + i8], c, mneg));
+        const float p = sgn(cc >> 1) * fast_exp2(fmaf(sacc[cc >> 1][8 * (cc & 1) + i8], c, mneg));
         psum += p;
         pf[cc][i8] = (__bf16)p;
       }
@@ -405,8 +460,8 @@ void attn_bf16_kernel(AttnArgs a) {
       if (t + 2 < 2 * KK) kread(t + 2);
       if (t < 16) {
         const int v = 2 * t, kb2 = v >> 4, rr = v & 15;
-        const float p0 = fast_exp2(fmaf(cur[kb2][rr], c, mneg));
-        const float p1 = fast_exp2(fmaf(cur[kb2][rr + 1], c, mneg));
+        const float p0 = sgn(kb2) * fast_exp2(fmaf(cur[kb2][rr], c, mneg));
+        const float p1 = sgn(kb2) * fast_exp2(fmaf(cur[kb2][rr + 1], c, mneg));
         psum0 += p0;
         psum1 += p1;
         pf[2 * kb2 + (rr >> 3)][rr & 7] = (__bf16)p0;
@@ -444,38 +499,72 @@ void attn_bf16_kernel(AttnArgs a) {
   // Software pipeline over the 4-slot ring: while the exponentials of tile it are computed on the
   // vector units, the matrix cores already form the scores of tile it+1; then tile it's products
   // with V. Tile t is loaded 3 tiles ahead into the slot that tile t-4 used.
+  if (!DELTA || ntile > 0) {  // (a stable-token pass over a sequence with no change has no tile)
 #pragma unroll
-  for (int s = 0; s < ST - 1; ++s)
-    if (s < ntile) issue(s, ring + s * SLOT);
-  if (ntile > 2) attn_wait_vm<2 * PER>();  // tile 0 landed
-  else if (ntile > 1) attn_wait_vm<PER>();
-  else attn_wait_vm<0>();
-  asm volatile("s_barrier" ::: "memory");
-  f32x16 sa[2], sb[2];
-  scores(ring, sa);
-  mask_tail(sa, t0);
-  bf16x8 pf[4];
-
-  for (int it = 0; it + 1 < ntile; ++it) {
-    // tile it+1 landed (the only later tile in flight is it+2); every wave finished tile it-1
-    if (it + 2 < ntile) attn_wait_vm<PER>();
+    for (int s = 0; s < ST - 1; ++s)
+      if (s < ntile) issue(s, ring + s * SLOT);
+    if (ntile > 2) attn_wait_vm<2 * PER>();  // tile 0 landed
+    else if (ntile > 1) attn_wait_vm<PER>();
     else attn_wait_vm<0>();
     asm volatile("s_barrier" ::: "memory");
-    if (it + 3 < ntile) issue(it + 3, ring + ((it + 3) % ST) * SLOT);
-    reference(sa);
-    scores_expo(ring + ((it + 1) % ST) * SLOT, sb, sa, pf);
-    pv(it % ST, pf);
-    mask_tail(sb, t0 + (it + 1) * kTK);
+    f32x16 sa[2], sb[2];
+    scores(ring, sa);
+    mask_tail(sa, 0);
+    bf16x8 pf[4];
+
+    for (int it = 0; it + 1 < ntile; ++it) {
+      // tile it+1 landed (the only later tile in flight is it+2); every wave finished tile it-1
+      if (it + 2 < ntile) attn_wait_vm<PER>();
+      else attn_wait_vm<0>();
+      asm volatile("s_barrier" ::: "memory");
+      if (it + 3 < ntile) issue(it + 3, ring + ((it + 3) % ST) * SLOT);
+      reference(sa);
+      scores_expo(ring + ((it + 1) % ST) * SLOT, sb, sa, pf);
+      pv(it % ST, pf);
+      mask_tail(sb, it + 1);
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) sa[kb2] = sb[kb2];
+      for (int kb2 = 0; kb2 < 2; ++kb2) sa[kb2] = sb[kb2];
+    }
+    reference(sa);
+    expo(sa, pf);
+    pv((ntile - 1) % ST, pf);
   }
-  reference(sa);
-  expo(sa, pf);
-  pv((ntile - 1) % ST, pf);
 
   // oacc[hb][rr] = unnormalised o[query n][hd 32 hb + 8 (rr/4) + 4 h + rr%4]
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
+  if constexpr (DELTA) {
+    // stored state scaled to this pass's reference point, plus the change of numerator and sum
+    const size_t sh = (size_t)qj * a.H + qh;
+    const float lf = a.st_l[sh] * fast_exp2(m_state - m_run);
+    const float l_new = lf + l_tot;
+    const float inv = 1.0f / l_new;
+    float* so = a.st_o + (size_t)qj * Nq + qh * HD;
+#pragma unroll
+    for (int hb = 0; hb < NB; ++hb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int e = 32 * hb + 8 * jj + 4 * h;
+        float o0[4];
+        Elem<float>::load4(so + e, o0);
+        const float v[4] = {(o0[0] * lf + oacc[hb][4 * jj]) * inv, (o0[1] * lf + oacc[hb][4 * jj + 1]) * inv,
+                            (o0[2] * lf + oacc[hb][4 * jj + 2]) * inv, (o0[3] * lf + oacc[hb][4 * jj + 3]) * inv};
+        Elem<float>::store4(so + e, v);
+        Elem<uint16_t>::store4(a.o_all + (size_t)qj * Nq + qh * HD + e, v);
+      }
+    if (h == 0) {
+      a.st_m[sh] = m_run;
+      a.st_l[sh] = l_new;
+    }
+    return;
+  }
+  // exact pass with the context of every token: the token's position, query and state
+  const int pos = a.st_o ? a.sel_idx[qj] : 0;
+  if (a.q_all && split == 0) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      *reinterpret_cast<bf16x8*>(a.q_all + (size_t)pos * Nq + qh * HD + 16 * kk + 8 * h) = qf[kk];
+  }
   if (a.nsplit == 1) {
     const float inv = 1.0f / l_tot;
 #pragma unroll
@@ -485,7 +574,15 @@ void attn_bf16_kernel(AttnArgs a) {
         const float v[4] = {oacc[hb][4 * jj] * inv, oacc[hb][4 * jj + 1] * inv,
                             oacc[hb][4 * jj + 2] * inv, oacc[hb][4 * jj + 3] * inv};
         Elem<uint16_t>::store4(a.o + (size_t)qj * Nq + qh * HD + 32 * hb + 8 * jj + 4 * h, v);
+        if (a.st_o) {
+          Elem<float>::store4(a.st_o + (size_t)pos * Nq + qh * HD + 32 * hb + 8 * jj + 4 * h, v);
+          Elem<uint16_t>::store4(a.o_all + (size_t)pos * Nq + qh * HD + 32 * hb + 8 * jj + 4 * h, v);
+        }
       }
+    if (a.st_o && h == 0) {
+      a.st_m[(size_t)pos * a.H + qh] = m_run;
+      a.st_l[(size_t)pos * a.H + qh] = l_tot;
+    }
   } else {
     const size_t base = ((size_t)split * a.m_cap + qj) * a.H + qh;
 #pragma unroll
@@ -529,6 +626,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const float inv = 1.0f / L;
   const float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
   Elem<uint16_t>::store4(a.o + (size_t)j * a.H * HD + h * HD + c, v);
+  if (a.st_o) {  // context of every token: state and context at the token's position
+    const size_t pos = (size_t)a.sel_idx[j];
+    Elem<float>::store4(a.st_o + pos * a.H * HD + h * HD + c, v);
+    Elem<uint16_t>::store4(a.o_all + pos * a.H * HD + h * HD + c, v);
+    if (c == 0) {
+      a.st_m[pos * a.H + h] = mmax;
+      a.st_l[pos * a.H + h] = L;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- float32 path (VALU)
@@ -621,12 +727,18 @@ template <int HD>
 static void launch_bf16(const AttnCfg& c, dim3 grid, const AttnArgs& a, hipStream_t st) {
   if constexpr (HD == 64) {
     if (c.nw == 4) {
-      hipLaunchKernelGGL((attn_bf16_kernel<HD, 4, 4>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<HD, 4, 4, false>), grid, dim3(256), 0, st, a);
       return;
     }
   }
-  hipLaunchKernelGGL((attn_bf16_kernel<HD, 8, 4>), grid, dim3(512), 0, st, a);
+  hipLaunchKernelGGL((attn_bf16_kernel<HD, 8, 4, false>), grid, dim3(512), 0, st, a);
 }
+
+// exact pass over the selected rows (plus, when `ctx` carries them, the state outputs)
+static hipError_t launch_exact_bf16(const ProjShape& s, float scale, const void* q_sel,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* row_ptr, void* o_sel, void* ws,
+                                    const AttnArgs& ctx, hipStream_t st);
 
 hipError_t launch_attn(bool bf16, const ProjShape& s, float scale, const void* q_sel,
                        const void* k_cache, const void* v_cache, const int32_t* sel_idx,
@@ -642,8 +754,16 @@ hipError_t launch_attn(bool bf16, const ProjShape& s, float scale, const void* q
       hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(256), 0, st, f);
     return hipGetLastError();
   }
+  AttnArgs none{};
+  return launch_exact_bf16(s, scale, q_sel, k_cache, v_cache, row_ptr, o_sel, ws, none, st);
+}
+
+static hipError_t launch_exact_bf16(const ProjShape& s, float scale, const void* q_sel,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* row_ptr, void* o_sel, void* ws,
+                                    const AttnArgs& ctx, hipStream_t st) {
   const AttnCfg c = plan_bf16(s);
-  AttnArgs a;
+  AttnArgs a = ctx;
   a.q = (const uint16_t*)q_sel; a.kc = (const uint16_t*)k_cache; a.vc = (const uint16_t*)v_cache;
   a.row_ptr = row_ptr; a.o = (uint16_t*)o_sel;
   a.B = s.B; a.S = s.S; a.H = s.H; a.Hkv = s.Hkv; a.m_cap = s.m_cap;
@@ -670,6 +790,74 @@ hipError_t launch_attn(bool bf16, const ProjShape& s, float scale, const void* q
     hipLaunchKernelGGL(attn_merge_kernel<64>, mg, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(attn_merge_kernel<128>, mg, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- context of every token
+// DyLLM (French summary page) §2.B: stable tokens reuse their previous attention weights and take
+// in only the changed keys (pass 1, every position), salient tokens are recomputed exactly against
+// the updated cache (pass 2, the selected rows; it overwrites what pass 1 wrote at their positions).
+hipError_t launch_salient_attn(const ProjShape& s, float scale, const void* q_sel, void* q_all,
+                               const void* k_cache, const void* v_cache, const void* k_old,
+                               const void* v_old, const int32_t* sel_idx, const int32_t* row_ptr,
+                               float* st_m, float* st_l, float* st_o, void* o_sel, void* o_all,
+                               void* ws, hipStream_t st) {
+  AttnArgs d{};
+  d.kc = (const uint16_t*)k_cache; d.vc = (const uint16_t*)v_cache;
+  d.row_ptr = row_ptr;
+  d.B = s.B; d.S = s.S; d.H = s.H; d.Hkv = s.Hkv; d.m_cap = s.m_cap;
+  d.nsplit = 1; d.kps = s.S;
+  d.scale_log2 = scale * kLog2e;
+  d.sel_idx = sel_idx; d.st_m = st_m; d.st_l = st_l; d.st_o = st_o;
+  d.o_all = (uint16_t*)o_all; d.q_all = (uint16_t*)q_all;
+  d.k_old = (const uint16_t*)k_old; d.v_old = (const uint16_t*)v_old;
+  const int G = s.H / s.Hkv;
+  const long rows = (long)s.S * G;
+  // eight waves (256 query rows) when that still gives a workgroup per CU, else four
+  const int nw = (long)s.B * s.Hkv * cdiv(rows, 256) >= 256 ? 8 : 4;
+  dim3 grid(s.B * s.Hkv, cdiv(rows, 32 * nw));
+  if (s.hd == 64) {
+    if (nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8, 4, true>), grid, dim3(512), 0, st, d);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, 4, 4, true>), grid, dim3(256), 0, st, d);
+  } else {
+    if (nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<128, 8, 4, true>), grid, dim3(512), 0, st, d);
+    else hipLaunchKernelGGL((attn_bf16_kernel<128, 4, 4, true>), grid, dim3(256), 0, st, d);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || s.m_cap == 0) return e;
+  return launch_exact_bf16(s, scale, q_sel, k_cache, v_cache, row_ptr, o_sel, ws, d, st);
+}
+
+// copies of the K/V rows at the selected positions: rows[j, hk, :] = cache[b, hk, s, :]
+__global__ __launch_bounds__(256) void gather_kv_rows_kernel(const uint4* kc, const uint4* vc,
+                                                             const int32_t* sel_idx,
+                                                             const int32_t* row_ptr, uint4* kr,
+                                                             uint4* vr, int B, int S, int Hkv,
+                                                             int m_cap, int chunks) {
+  const int M = min(row_ptr[B], m_cap);
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;  // one 16-byte chunk of K and of V
+  const size_t per_row = (size_t)Hkv * chunks;
+  const int j = (int)(idx / per_row);
+  if (j >= M) return;
+  const int rest = (int)(idx - (size_t)j * per_row);
+  const int hk = rest / chunks, c = rest - hk * chunks;
+  const int id = sel_idx[j];
+  const int b = id / S, sp = id - b * S;
+  const size_t src = (((size_t)b * Hkv + hk) * S + sp) * chunks + c;
+  kr[idx] = kc[src];
+  vr[idx] = vc[src];
+}
+
+hipError_t launch_gather_kv_rows(const ProjShape& s, size_t elem, const void* k_cache,
+                                 const void* v_cache, const int32_t* sel_idx,
+                                 const int32_t* row_ptr, void* k_rows, void* v_rows,
+                                 hipStream_t st) {
+  if (s.m_cap == 0) return hipSuccess;
+  const int chunks = (int)(s.hd * elem / 16);
+  const size_t threads = (size_t)s.m_cap * s.Hkv * chunks;
+  hipLaunchKernelGGL(gather_kv_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     st, (const uint4*)k_cache, (const uint4*)v_cache, sel_idx, row_ptr,
+                     (uint4*)k_rows, (uint4*)v_rows, s.B, s.S, s.Hkv, s.m_cap, chunks);
   return hipGetLastError();
 }
 
