@@ -39,10 +39,16 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="llada_layer", choices=["llada_layer", "llada_step"],
+    p.add_argument("--workload", default="llada_layer",
+                   choices=["llada_layer", "llada_step", "llada_context"],
                    help="llada_layer: one LLaDA-8B-shaped layer, B=1 (default); llada_step: the "
-                        "full 32-layer early-skip step, B=8, S=1024, top-205 per sequence")
+                        "full 32-layer early-skip step, B=8, S=1024, top-205 per sequence; "
+                        "llada_context: the llada_layer step keeping the attention context of "
+                        "every token (exact rows for the selected, changed-key update for the rest)")
     p.add_argument("--sets", type=int, default=16, help="rotated input/weight sets")
+    p.add_argument("--context-seq", type=int, default=1024, choices=[1024, 4096],
+                   help="llada_context: sequence length (1024: top-128 of the llada_layer "
+                        "recipe; 4096: the long-context shape with the top-96)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget of the CPU oracle sample (0 = skip)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -95,6 +101,9 @@ def main():
 
     if args.workload == "llada_step":
         run_llada_step(args)
+        return
+    if args.workload == "llada_context":
+        run_llada_context(args)
         return
 
     import token_skipping_partial_amd as tsp  # raises if libdllm.so is not built
@@ -298,6 +307,137 @@ def run_llada_step(args):
         "config": {"workload": "llada_step: 32 LLaDA-8B-shaped layers, B=8, S=1024, early skip at "
                                "layer 4, alpha=0.5, top-205 per sequence",
                    "units_per_step": units, "selected_per_step": M},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_llada_context(args):
+    """The llada_layer step with the attention context of every token kept (DyLLM §2.B): copies
+    of the rows about to change, the projection, then exact rows for the 128 selected tokens and
+    the changed-key update of the other 896 tokens' softmax state, then the FFN of the selected.
+    16 rotated sets, each with its own caches, query cache and state (initialised untimed by a
+    select-all call)."""
+    import token_skipping_partial_amd as tsp
+    from synth import workloads as W
+    from token_skipping_partial_amd.step import (LayerScratch, LayerWeights, SelectConfig,
+                                                 SingleLayerStep, all_rows, selected_layer)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    if args.context_seq == 4096:
+        dims, k_sel, n_large = W.LLADA_LONG, 96, round(0.15 * 4096)
+    else:
+        dims, k_sel, n_large = W.LLADA_LAYER, W.LLADA_TOPK, W.LLADA_LARGE
+    shape = tsp.Shape(B=dims.B, S=dims.S, d=dims.d, H=dims.H, Hkv=dims.Hkv, hd=dims.hd,
+                      F=dims.F, dtype="bf16", V=dims.V)
+    ntok, nq, nkv = dims.B * dims.S, dims.H * dims.hd, dims.Hkv * dims.hd
+    scale = 1.0 / math.sqrt(dims.hd)
+    print(f"[bench] llada_context: building {args.sets} sets of {shape}", file=sys.stderr,
+          flush=True)
+    fill = LayerScratch(shape, ntok, dev)
+    sel_all, rp_all = all_rows(shape, dev)
+    ws_all = tsp.workspace(tsp.OP_ATTN, shape, ntok)
+    sets = []
+    for i in range(args.sets):
+        h_prev, h_cur, _, logits, w = W.layer_inputs(dims, n_large, seed=9000 + i, device=dev)
+        wd = LayerWeights.from_dict(w, dev)
+        kc = torch.zeros(dims.B, dims.Hkv, dims.S, dims.hd, dtype=dims.dtype, device=dev)
+        vc = torch.zeros_like(kc)
+        h_out = torch.zeros(dims.B, dims.S, dims.d, dtype=dims.dtype, device=dev)
+        selected_layer(shape, wd, h_prev, kc, vc, h_out, sel_all, rp_all, fill)
+        q_all = torch.empty(ntok, nq, dtype=dims.dtype, device=dev)
+        st_m = torch.empty(ntok, dims.H, device=dev)
+        st_l = torch.empty(ntok, dims.H, device=dev)
+        st_o = torch.empty(ntok, nq, device=dev)
+        o_all = torch.empty(ntok, nq, dtype=dims.dtype, device=dev)
+        # state of step t-1: every token's context from its query of the fill pass
+        kv_rows = torch.empty(2, ntok, nkv, dtype=dims.dtype, device=dev)
+        tsp.dllm_salient_attn(shape, scale, fill.q_sel, q_all, kc, vc, kv_rows[0], kv_rows[1],
+                              sel_all, rp_all, ntok, st_m, st_l, st_o, fill.o_sel, o_all, ws_all)
+        sets.append((wd, h_prev, h_cur, logits, kc, vc, h_out, q_all, st_m, st_l, st_o, o_all))
+    del fill, kv_rows
+    torch.cuda.synchronize()
+    step = SingleLayerStep(shape, SelectConfig(mode=tsp.SEL_TOPK, k=k_sel, alpha=0.5), k_sel, dev)
+    sc = step.scratch
+    k_old = torch.empty(k_sel, nkv, dtype=dims.dtype, device=dev)
+    v_old = torch.empty_like(k_old)
+    stream = torch.cuda.current_stream()
+
+    def run(i, ev=None):
+        wd, h_prev, h_cur, logits, kc, vc, h_out, q_all, st_m, st_l, st_o, o_all = \
+            sets[i % len(sets)]
+        rec = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
+        rec(0)
+        tsp.dllm_saliency(shape, tsp.DELTA_L1N, 0.5, h_cur, h_prev, logits, step.score)
+        tsp.dllm_select_compact(shape, tsp.SEL_TOPK, 0.0, k_sel, step.score, None, step.sel_idx,
+                                step.row_ptr)
+        rec(1)
+        tsp.dllm_gather_kv_rows(shape, kc, vc, step.sel_idx, step.row_ptr, k_sel, k_old, v_old)
+        rec(2)
+        tsp.dllm_gather_qkv_scatter_kv(shape, h_cur, wd.g_attn, wd.w_qkv, step.sel_idx,
+                                       step.row_ptr, k_sel, sc.q_sel, kc, vc, sc.ws_qkv)
+        rec(3)
+        tsp.dllm_salient_attn(shape, scale, sc.q_sel, q_all, kc, vc, k_old, v_old, step.sel_idx,
+                              step.row_ptr, k_sel, st_m, st_l, st_o, sc.o_sel, o_all, sc.ws_attn)
+        rec(4)
+        tsp.dllm_gather_ffn_scatter(shape, h_cur, sc.o_sel, wd.w_o, wd.g_ffn, wd.w_gate, wd.w_up,
+                                    wd.w_down, step.sel_idx, step.row_ptr, k_sel, h_out, sc.ws_ffn)
+        rec(5)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        run(args.warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    M = int(step.row_ptr[-1].item())
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        run(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
+    names = ["saliency+select", "gather_kv_rows", "gather_qkv_scatter_kv", "salient_attn",
+             "gather_ffn_scatter"]
+    per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+           for j, n in enumerate(names)}
+    # what the same contexts cost by exact recomputation of every row (dllm_partial_attn, all
+    # 1024 queries against all keys), timed on one set
+    wd, h_prev, h_cur, logits, kc, vc, h_out, q_all, st_m, st_l, st_o, o_all = sets[0]
+    o_full = torch.empty(ntok, nq, dtype=dims.dtype, device=dev)
+    for _ in range(3):
+        tsp.dllm_partial_attn(shape, scale, q_all, kc, vc, sel_all, rp_all, ntok, o_full, ws_all)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        tsp.dllm_partial_attn(shape, scale, q_all, kc, vc, sel_all, rp_all, ntok, o_full, ws_all)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    full_ms = e0.elapsed_time(e1) / 10
+    b = 2
+    ctx_bytes = (ntok * nq * b                       # query cache
+                 + 2 * ntok * nq * 4 + 4 * ntok * dims.H * 4   # state read + write
+                 + ntok * nq * b                     # context of every token
+                 + 2 * 2 * M * nkv * b               # old and new rows of the changed keys
+                 + M * nq * b * 3                    # new queries, their cache rows, o_sel
+                 + 2 * dims.B * dims.S * nkv * b)    # exact rows: the cache once per kv head
+    gbs = ctx_bytes / (per["salient_attn"] * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(M * args.steps / (ms * args.steps * 1e-3), 1),
+        "unit": "selected-token layer-steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: as llada_layer",
+        "config": {"workload": f"llada_context: LLaDA-8B-shaped layer step, B=1, S={dims.S}, "
+                               f"top-{k_sel}, keeping the attention context of every token "
+                               f"({k_sel} exact rows, {ntok - k_sel} changed-key updates)",
+                   "selected_per_step": M, "rotated_sets": args.sets},
+        "salient_attn": {"ms": round(per["salient_attn"], 4), "bytes": ctx_bytes,
+                         "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "all_rows_exact_ms": round(full_ms, 4)},
+        "kernels": {k: round(v, 4) for k, v in per.items()},
     }
     print(json.dumps(out), flush=True)
 
