@@ -15,6 +15,7 @@
  *
  *   dllm_gather_kv_rows         copies of the K/V rows a projection call is about to overwrite
  *   dllm_salient_attn           exact rows for the selected tokens, changed-key update for the rest
+ *   dllm_gather_rows            compact copies of selected rows (e.g. contexts for the FFN call)
  *
  * Sources (web pages; section names as printed there):
  *   [ES-dLLM]  "ES-dLLM: Efficient Inference for Diffusion Large Language Models by Early-Skipping",
@@ -208,6 +209,16 @@ dllm_status dllm_salient_attn(const dllm_shape* shape, float scale, const void* 
                               const int32_t* row_ptr, int32_t m_cap, float* st_m, float* st_l,
                               float* st_o, void* o_sel, void* o_all, void* ws, size_t ws_bytes,
                               void* stream);
+
+/* Compact copies of whole rows [DyLLM §2.A: the FFN runs for the tokens whose context changed;
+ * this gathers their contexts from the context of every token into the compact rows the FFN call
+ * reads]. For j < M = min(row_ptr[B], m_cap): dst[j, :] = src[sel_idx[j], :], rows of `width`
+ * elements of shape->dtype (only B, S and dtype of `shape` are used). src : [B*S, width];
+ * dst : [m_cap, width]. width * element size must be a multiple of 16 bytes. Bit-exact copies.
+ * Workspace: none. */
+dllm_status dllm_gather_rows(const dllm_shape* shape, const void* src, int32_t width,
+                             const int32_t* sel_idx, const int32_t* row_ptr, int32_t m_cap,
+                             void* dst, void* stream);
 
 /* Bytes of device workspace the call `op` (a dllm_op) needs for this shape and m_cap; 0 when
  * none. Returns (size_t)-1 for an invalid op or shape. Pure host function. */

@@ -169,3 +169,12 @@ def test_context_call_validation():
     st = lib.dllm_salient_attn(ctypes.byref(s), 0.1, P, P, P, P, P, P, P, P, 128, P, P, P, P, P,
                                P, need - 1, None)
     assert st == tsp.DLLM_ERR_WORKSPACE
+
+
+def test_gather_rows_validation():
+    s = llada()
+    g = tsp.dllm_gather_rows
+    assert rc(g, s, None, 4096, P, P, 128, P) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(g, s, P, 0, P, P, 128, P) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(g, s, P, 4096, P, P, 1025, P) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(g, s, P, 4, P, P, 128, P) == tsp.DLLM_ERR_UNSUPPORTED   # 8-byte rows

@@ -28,7 +28,8 @@ MAX_SALIENT_S = 8192
 
 EXPORTS = ("dllm_saliency", "dllm_select_compact", "dllm_gather_qkv_scatter_kv",
            "dllm_partial_attn", "dllm_gather_ffn_scatter", "dllm_gather_kv_rows",
-           "dllm_salient_attn", "dllm_workspace_bytes", "dllm_status_string", "dllm_version")
+           "dllm_salient_attn", "dllm_gather_rows", "dllm_workspace_bytes", "dllm_status_string",
+           "dllm_version")
 
 
 class DllmError(RuntimeError):
@@ -61,7 +62,7 @@ class Shape(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m token_skipping_partial_amd.build`"
+        raise ImportError(f"{LIB_PATH} is not built; run `python token_skipping_partial_amd/build.py`"
                           " (or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -74,6 +75,7 @@ def _load():
         "dllm_gather_ffn_scatter": (I32, [SP, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]),
         "dllm_gather_kv_rows": (I32, [SP, P, P, P, P, I32, P, P, P]),
         "dllm_salient_attn": (I32, [SP, F, P, P, P, P, P, P, P, P, I32, P, P, P, P, P, P, SZ, P]),
+        "dllm_gather_rows": (I32, [SP, P, I32, P, P, I32, P, P]),
         "dllm_workspace_bytes": (SZ, [I32, SP, I32]),
         "dllm_status_string": (ctypes.c_char_p, [I32]),
         "dllm_version": (I32, []),
@@ -195,3 +197,9 @@ def dllm_salient_attn(shape, scale, q_sel, q_all, k_cache, v_cache, k_old, v_old
                                   _ptr(sel_idx), _ptr(row_ptr), int(m_cap), _ptr(st_m),
                                   _ptr(st_l), _ptr(st_o), _ptr(o_sel), _ptr(o_all), wp, wn,
                                   _stream(stream)), "dllm_salient_attn")
+
+
+def dllm_gather_rows(shape, src, width, sel_idx, row_ptr, m_cap, dst, stream=None):
+    _check(_lib.dllm_gather_rows(ctypes.byref(shape), _ptr(src), int(width), _ptr(sel_idx),
+                                 _ptr(row_ptr), int(m_cap), _ptr(dst), _stream(stream)),
+           "dllm_gather_rows")

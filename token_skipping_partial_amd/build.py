@@ -1,6 +1,9 @@
 """Compile the HIP sources into the in-tree shared library `libdllm.so` (gfx950 only).
 
-    python -m token_skipping_partial_amd.build
+    python token_skipping_partial_amd/build.py
+
+(run as a script, or through __graft_entry__.build(): importing the package first would load the
+library that is about to be rebuilt).
 
 hipcc cross-compiles for gfx950 without a GPU present. Packed fp32 instructions are disabled
 (-packed-fp32-ops) for every device compilation.

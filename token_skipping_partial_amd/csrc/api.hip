@@ -242,4 +242,17 @@ dllm_status dllm_salient_attn(const dllm_shape* shape, float scale, const void* 
                                         (hipStream_t)stream));
 }
 
+dllm_status dllm_gather_rows(const dllm_shape* shape, const void* src, int32_t width,
+                             const int32_t* sel_idx, const int32_t* row_ptr, int32_t m_cap,
+                             void* dst, void* stream) {
+  if (!base_shape_ok(shape) || width <= 0 || m_cap < 0 || (long)m_cap > (long)shape->B * shape->S)
+    return DLLM_ERR_INVALID_ARG;
+  if (!src || !sel_idx || !row_ptr || !dst || !aligned16(src) || !aligned16(dst))
+    return DLLM_ERR_INVALID_ARG;
+  const size_t row_bytes = (size_t)width * (shape->dtype == DLLM_BF16 ? 2 : 4);
+  if (row_bytes % 16 != 0) return DLLM_ERR_UNSUPPORTED;
+  return hip_status(launch_gather_rows(shape->B, m_cap, row_bytes, src, sel_idx, row_ptr, dst,
+                                       (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -861,4 +861,27 @@ hipError_t launch_gather_kv_rows(const ProjShape& s, size_t elem, const void* k_
   return hipGetLastError();
 }
 
+// compact copies of whole rows: dst[j, :] = src[sel_idx[j], :] (16-byte chunks per row)
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* src, const int32_t* sel_idx,
+                                                          const int32_t* row_ptr, uint4* dst,
+                                                          int B, int m_cap, int chunks) {
+  const int M = min(row_ptr[B], m_cap);
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int j = (int)(idx / chunks);
+  if (j >= M) return;
+  const int c = (int)(idx - (size_t)j * chunks);
+  dst[idx] = src[(size_t)sel_idx[j] * chunks + c];
+}
+
+hipError_t launch_gather_rows(int B, int m_cap, size_t row_bytes, const void* src,
+                              const int32_t* sel_idx, const int32_t* row_ptr, void* dst,
+                              hipStream_t st) {
+  if (m_cap == 0) return hipSuccess;
+  const int chunks = (int)(row_bytes / 16);
+  const size_t threads = (size_t)m_cap * chunks;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     st, (const uint4*)src, sel_idx, row_ptr, (uint4*)dst, B, m_cap, chunks);
+  return hipGetLastError();
+}
+
 }  // namespace dllm

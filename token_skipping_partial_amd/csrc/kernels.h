@@ -86,4 +86,7 @@ hipError_t launch_gather_kv_rows(const ProjShape& s, size_t elem, const void* k_
                                  const int32_t* row_ptr, void* k_rows, void* v_rows,
                                  hipStream_t st);
 constexpr int kSalientMaxS = 8192;  // sequence length limit of the stable-token pass
+hipError_t launch_gather_rows(int B, int m_cap, size_t row_bytes, const void* src,
+                              const int32_t* sel_idx, const int32_t* row_ptr, void* dst,
+                              hipStream_t st);
 }  // namespace dllm
