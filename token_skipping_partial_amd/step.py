@@ -6,6 +6,9 @@ saliency -> selection -> one selected layer. A multi-layer early-skip step runs 
 skip layer on every token, scores tokens at the skip layer, selects once, and runs the remaining
 layers on the selected rows against the cached K/V (ES-dLLM, German summary page §2.B: skipping
 at early layers such as 1/8 of the depth; the selection is reused by the layers above it).
+A layer-adaptive step (DyLLM, French summary page §2.A and §2.B) keeps the attention context of
+every token in every layer and lets each layer pick, by the cosine change of the contexts, the
+tokens whose FFN is recomputed; those tokens' changed outputs decide the next layer's rows.
 """
 from __future__ import annotations
 
@@ -14,8 +17,9 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import (OP_ATTN, OP_FFN, OP_QKV, SEL_THRESHOLD, SEL_TOPK, Shape, dllm_gather_ffn_scatter,
-               dllm_gather_qkv_scatter_kv, dllm_partial_attn, dllm_saliency,
+from . import (DELTA_COS, DELTA_L1N, OP_ATTN, OP_FFN, OP_QKV, SEL_THRESHOLD, SEL_TOPK, Shape,
+               dllm_gather_ffn_scatter, dllm_gather_kv_rows, dllm_gather_qkv_scatter_kv,
+               dllm_gather_rows, dllm_partial_attn, dllm_saliency, dllm_salient_attn,
                dllm_select_compact, workspace)
 
 
@@ -161,3 +165,100 @@ class EarlySkipModel:
             selected_layer(self.shape, self.layers[l], self.hidden[l], self.k[l], self.v[l],
                            self.hidden[l + 1], s.sel_idx, s.row_ptr, self.sparse, stream)
         return s.sel_idx, s.row_ptr
+
+
+class LayerAdaptiveModel:
+    """L-layer step that keeps the attention context of every token (DyLLM, French summary page
+    §2.A layer-adaptive saliency, §2.B salient / approximate attention).
+
+    Per layer l and step t, with A_l the tokens whose layer input changed:
+      copies of the K/V rows of A_l; QKV of A_l into the caches; contexts of every token
+      (`dllm_salient_attn`: exact for A_l, changed-key update for the rest); the cosine change of
+      each token's context against step t-1 (`dllm_saliency`, cosine kind, alpha 0); the tokens
+      above the threshold (`dllm_select_compact`, threshold mode) get W_o + FFN and write their
+      row of hidden[l + 1]; the others keep last step's row. A_{l+1} is that set. A_0 is chosen
+      by the L1-normalised change of the layer-0 input against step t-1 (threshold `tau_in`).
+    Buffers are sized for every token (the thresholded counts are only known on the device).
+    """
+
+    def __init__(self, shape: Shape, layers: list, tau_in: float, tau_ctx, scale=None,
+                 device="cuda"):
+        self.shape, self.layers = shape, layers
+        self.tau_in = tau_in
+        self.scale = attn_scale(shape) if scale is None else scale
+        L = len(layers)
+        self.tau_ctx = list(tau_ctx) if isinstance(tau_ctx, (list, tuple)) else [tau_ctx] * L
+        B, S, d, H, Hkv, hd = shape.B, shape.S, shape.d, shape.H, shape.Hkv, shape.hd
+        dt = shape.torch_dtype
+        ntok, nq = B * S, H * hd
+        z = lambda *sh, dtype=dt: torch.zeros(*sh, dtype=dtype, device=device)  # noqa: E731
+        self.k = [z(B, Hkv, S, hd) for _ in range(L)]
+        self.v = [z(B, Hkv, S, hd) for _ in range(L)]
+        self.hidden = [z(B, S, d) for _ in range(L + 1)]
+        self.x_ref = z(B, S, d)                       # layer-0 input at step t-1
+        self.q_all = [z(ntok, nq) for _ in range(L)]
+        self.st_m = [z(ntok, H, dtype=torch.float32) for _ in range(L)]
+        self.st_l = [z(ntok, H, dtype=torch.float32) for _ in range(L)]
+        self.st_o = [z(ntok, nq, dtype=torch.float32) for _ in range(L)]
+        self.ctx = [[z(ntok, nq), z(ntok, nq)] for _ in range(L)]  # contexts at t and t-1
+        self.cur = 0                                  # index of the step-t context buffer
+        self.ctx_shape = Shape(B=B, S=S, d=nq, H=H, Hkv=Hkv, hd=hd, F=shape.F,
+                               dtype=shape.dtype, V=0)
+        self.scratch = LayerScratch(shape, ntok, device)
+        self.k_old = z(ntok, Hkv * hd)
+        self.v_old = z(ntok, Hkv * hd)
+        self.o_rows = z(ntok, nq)
+        self.score = torch.empty(B, S, dtype=torch.float32, device=device)
+        # row sets: [0] input-change set, then one per layer (its FFN set = next layer's input set)
+        self.sel = [torch.empty(ntok, dtype=torch.int32, device=device) for _ in range(L + 1)]
+        self.rp = [torch.empty(B + 1, dtype=torch.int32, device=device) for _ in range(L + 1)]
+        self.all_sel, self.all_rp = all_rows(shape, device)
+
+    def _layer(self, l, sel_a, rp_a, sel_f, rp_f, tau, stream):
+        sh, w, sc, n = self.shape, self.layers[l], self.scratch, self.shape.B * self.shape.S
+        cur, prev = self.ctx[l][self.cur], self.ctx[l][1 - self.cur]
+        dllm_gather_kv_rows(sh, self.k[l], self.v[l], sel_a, rp_a, n, self.k_old, self.v_old,
+                            stream)
+        dllm_gather_qkv_scatter_kv(sh, self.hidden[l], w.g_attn, w.w_qkv, sel_a, rp_a, n,
+                                   sc.q_sel, self.k[l], self.v[l], sc.ws_qkv, stream)
+        dllm_salient_attn(sh, self.scale, sc.q_sel, self.q_all[l], self.k[l], self.v[l],
+                          self.k_old, self.v_old, sel_a, rp_a, n, self.st_m[l], self.st_l[l],
+                          self.st_o[l], sc.o_sel, cur, sc.ws_attn, stream)
+        if tau is None:   # every token (fill)
+            sel_f.copy_(self.all_sel)
+            rp_f.copy_(self.all_rp)
+        else:
+            dllm_saliency(self.ctx_shape, DELTA_COS, 0.0, cur, prev, None, self.score,
+                          stream=stream)
+            dllm_select_compact(sh, SEL_THRESHOLD, tau, 0, self.score, None, sel_f, rp_f,
+                                stream=stream)
+        dllm_gather_rows(self.ctx_shape, cur, self.ctx_shape.d, sel_f, rp_f, n, self.o_rows,
+                         stream)
+        dllm_gather_ffn_scatter(sh, self.hidden[l], self.o_rows, w.w_o, w.g_ffn, w.w_gate,
+                                w.w_up, w.w_down, sel_f, rp_f, n, self.hidden[l + 1], sc.ws_ffn,
+                                stream)
+
+    def fill(self, x0, stream=None):
+        """Step 0: every layer on every token; primes caches, states and both context buffers."""
+        self.hidden[0].copy_(x0)
+        self.x_ref.copy_(x0)
+        for l in range(len(self.layers)):
+            self._layer(l, self.all_sel, self.all_rp, self.sel[l + 1], self.rp[l + 1], None,
+                        stream)
+            self.ctx[l][1 - self.cur].copy_(self.ctx[l][self.cur])
+
+    def step(self, x, tau_ctx=None, stream=None):
+        """One denoising step on layer-0 input x (optionally with this step's per-layer context
+        thresholds); returns the row sets: [0] input change, [l + 1] FFN rows of layer l."""
+        taus = self.tau_ctx if tau_ctx is None else list(tau_ctx)
+        self.cur = 1 - self.cur
+        self.hidden[0].copy_(x)
+        dllm_saliency(self.shape, DELTA_L1N, 0.0, self.hidden[0], self.x_ref, None, self.score,
+                      stream=stream)
+        dllm_select_compact(self.shape, SEL_THRESHOLD, self.tau_in, 0, self.score, None,
+                            self.sel[0], self.rp[0], stream=stream)
+        self.x_ref.copy_(x)
+        for l in range(len(self.layers)):
+            self._layer(l, self.sel[l], self.rp[l], self.sel[l + 1], self.rp[l + 1], taus[l],
+                        stream)
+        return self.sel, self.rp
