@@ -40,11 +40,13 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llada_layer",
-                   choices=["llada_layer", "llada_step", "llada_context"],
+                   choices=["llada_layer", "llada_step", "llada_context", "llada_adaptive"],
                    help="llada_layer: one LLaDA-8B-shaped layer, B=1 (default); llada_step: the "
                         "full 32-layer early-skip step, B=8, S=1024, top-205 per sequence; "
                         "llada_context: the llada_layer step keeping the attention context of "
-                        "every token (exact rows for the selected, changed-key update for the rest)")
+                        "every token (exact rows for the selected, changed-key update for the rest); "
+                        "llada_adaptive: 32 LLaDA-8B layers, B=1, S=1024, per-layer FFN rows chosen "
+                        "by the cosine change of every token's attention context")
     p.add_argument("--sets", type=int, default=16, help="rotated input/weight sets")
     p.add_argument("--context-seq", type=int, default=1024, choices=[1024, 4096],
                    help="llada_context: sequence length (1024: top-128 of the llada_layer "
@@ -104,6 +106,9 @@ def main():
         return
     if args.workload == "llada_context":
         run_llada_context(args)
+        return
+    if args.workload == "llada_adaptive":
+        run_llada_adaptive(args)
         return
 
     import token_skipping_partial_amd as tsp  # raises if libdllm.so is not built
@@ -438,6 +443,74 @@ def run_llada_context(args):
                          "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "all_rows_exact_ms": round(full_ms, 4)},
         "kernels": {k: round(v, 4) for k, v in per.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_llada_adaptive(args):
+    """32 LLaDA-8B layers, B=1, S=1024, layer-adaptive (DyLLM §2.A/§2.B): the 154 tokens whose
+    layer-0 input moved (L1-normalised change > 0.05) are the first layer's rows; in every layer
+    the contexts of all tokens are kept and the tokens whose context moved most (cosine change
+    above a per-layer threshold, set from an untimed calibration step at the 80th percentile of
+    that layer's scores) get W_o + FFN and become the next layer's rows. Inputs cumulative as in
+    llada_step."""
+    import synth
+    import token_skipping_partial_amd as tsp
+    from synth import workloads as W
+    from token_skipping_partial_amd.step import LayerAdaptiveModel, LayerWeights
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dims, L = W.LLADA_LAYER, 32
+    shape = tsp.Shape(B=dims.B, S=dims.S, d=dims.d, H=dims.H, Hkv=dims.Hkv, hd=dims.hd,
+                      F=dims.F, dtype="bf16", V=dims.V)
+    print(f"[bench] llada_adaptive: {L} layers of {shape}", file=sys.stderr, flush=True)
+    layers = [LayerWeights.from_dict(synth.layer_weights(dims.d, dims.H, dims.Hkv, dims.hd, dims.F,
+                                                         seed=7000 + l, device="cuda"))
+              for l in range(L)]
+    model = LayerAdaptiveModel(shape, layers, 0.05, [0.0] * L)
+    nsteps = args.warmup + args.steps + 1
+    xs = [synth.normal((dims.B, dims.S, dims.d), 1.0, 7500, torch.bfloat16, "cuda")]
+    for t in range(1, nsteps + 1):
+        large = synth.large_positions(dims.B, dims.S, W.LLADA_LARGE, seed=7600 + t, device="cuda")
+        xs.append(synth.perturb(xs[-1], large, seed=7700 + t))
+    model.fill(xs[0])
+    # calibration (untimed): context thresholds at the 80th percentile of each layer's scores
+    taus = []
+    model.layer_scores = None
+    for l in range(L):
+        model.step(xs[1], tau_ctx=taus + [-1.0] * (L - l), record=True)
+        taus.append(float(torch.quantile(model.layer_scores[l].flatten(), 0.8).item()))
+        model.fill(xs[0])
+    model.tau_ctx = taus
+    for t in range(args.warmup):
+        model.step(xs[1 + t])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    counts = []
+    t0.record(stream)
+    for t in range(args.steps):
+        sel, rp = model.step(xs[1 + args.warmup + t])
+        counts.append(torch.stack([r[-1] for r in rp]))
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    c = torch.stack(counts).float().mean(0).cpu().tolist()   # [input rows, FFN rows per layer]
+    ffn_rows = sum(c[1:])
+    qkv_rows = sum(c[:-1])
+    out = {
+        "metric": METRIC, "value": round(ffn_rows / (ms * 1e-3), 1),
+        "unit": "selected-token layer-steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: X0 N(0,1), per step 154 tokens + N(0,0.5^2), rest + N(0,(1e-3)^2); "
+                "random-init weights N(0,0.02^2)",
+        "config": {"workload": "llada_adaptive: 32 LLaDA-8B-shaped layers, B=1, S=1024, "
+                               "layer-adaptive FFN rows (cosine change of every token's context, "
+                               "per-layer threshold at the calibrated 80th percentile)",
+                   "ffn_rows_per_step": round(ffn_rows, 1),
+                   "projection_rows_per_step": round(qkv_rows, 1),
+                   "rows_per_layer": [round(v, 1) for v in c]},
     }
     print(json.dumps(out), flush=True)
 

@@ -213,6 +213,7 @@ class LayerAdaptiveModel:
         self.sel = [torch.empty(ntok, dtype=torch.int32, device=device) for _ in range(L + 1)]
         self.rp = [torch.empty(B + 1, dtype=torch.int32, device=device) for _ in range(L + 1)]
         self.all_sel, self.all_rp = all_rows(shape, device)
+        self.layer_scores = None  # per-layer copies of the context scores (step(record=True))
 
     def _layer(self, l, sel_a, rp_a, sel_f, rp_f, tau, stream):
         sh, w, sc, n = self.shape, self.layers[l], self.scratch, self.shape.B * self.shape.S
@@ -230,6 +231,8 @@ class LayerAdaptiveModel:
         else:
             dllm_saliency(self.ctx_shape, DELTA_COS, 0.0, cur, prev, None, self.score,
                           stream=stream)
+            if self.layer_scores is not None:
+                self.layer_scores[l].copy_(self.score)
             dllm_select_compact(sh, SEL_THRESHOLD, tau, 0, self.score, None, sel_f, rp_f,
                                 stream=stream)
         dllm_gather_rows(self.ctx_shape, cur, self.ctx_shape.d, sel_f, rp_f, n, self.o_rows,
@@ -247,10 +250,15 @@ class LayerAdaptiveModel:
                         stream)
             self.ctx[l][1 - self.cur].copy_(self.ctx[l][self.cur])
 
-    def step(self, x, tau_ctx=None, stream=None):
+    def step(self, x, tau_ctx=None, record=False, stream=None):
         """One denoising step on layer-0 input x (optionally with this step's per-layer context
-        thresholds); returns the row sets: [0] input change, [l + 1] FFN rows of layer l."""
+        thresholds); returns the row sets: [0] input change, [l + 1] FFN rows of layer l.
+        record=True keeps each layer's context scores in `layer_scores`."""
         taus = self.tau_ctx if tau_ctx is None else list(tau_ctx)
+        if record and self.layer_scores is None:
+            self.layer_scores = [torch.empty_like(self.score) for _ in self.layers]
+        elif not record:
+            self.layer_scores = None
         self.cur = 1 - self.cur
         self.hidden[0].copy_(x)
         dllm_saliency(self.shape, DELTA_L1N, 0.0, self.hidden[0], self.x_ref, None, self.score,
