@@ -600,8 +600,9 @@ void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// fixed-order log-sum-exp merge of the key-split partials; one thread per 4 output columns
-template <int HD>
+// fixed-order log-sum-exp merge of the key-split partials; one thread per 4 output columns.
+// NS > 0: exactly NS splits, every partial loaded before the merge; NS == 0: a.nsplit of them.
+template <int HD, int NS = 0>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int M = min(a.row_ptr[a.B], a.m_cap);
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -612,16 +613,35 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int h = (int)(jh - (size_t)j * a.H);
   const int c = (int)(idx - jh * QG) * 4;
   float mmax = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s)
-    mmax = fmaxf(mmax, a.part_ml[(((size_t)s * a.m_cap + j) * a.H + h) * 2]);
   float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.nsplit; ++s) {
-    const size_t base = ((size_t)s * a.m_cap + j) * a.H + h;
-    const float w = fast_exp2(a.part_ml[base * 2] - mmax);
-    L += w * a.part_ml[base * 2 + 1];
-    float p[4];
-    Elem<float>::load4(a.part_o + base * HD + c, p);
-    o[0] += w * p[0]; o[1] += w * p[1]; o[2] += w * p[2]; o[3] += w * p[3];
+  if constexpr (NS > 0) {
+    float2 ml[NS];
+    float p[NS][4];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const size_t base = ((size_t)s * a.m_cap + j) * a.H + h;
+      ml[s] = *reinterpret_cast<const float2*>(a.part_ml + base * 2);
+      Elem<float>::load4(a.part_o + base * HD + c, p[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) mmax = fmaxf(mmax, ml[s].x);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float w = fast_exp2(ml[s].x - mmax);
+      L += w * ml[s].y;
+      o[0] += w * p[s][0]; o[1] += w * p[s][1]; o[2] += w * p[s][2]; o[3] += w * p[s][3];
+    }
+  } else {
+    for (int s = 0; s < a.nsplit; ++s)
+      mmax = fmaxf(mmax, a.part_ml[(((size_t)s * a.m_cap + j) * a.H + h) * 2]);
+    for (int s = 0; s < a.nsplit; ++s) {
+      const size_t base = ((size_t)s * a.m_cap + j) * a.H + h;
+      const float w = fast_exp2(a.part_ml[base * 2] - mmax);
+      L += w * a.part_ml[base * 2 + 1];
+      float p[4];
+      Elem<float>::load4(a.part_o + base * HD + c, p);
+      o[0] += w * p[0]; o[1] += w * p[1]; o[2] += w * p[2]; o[3] += w * p[3];
+    }
   }
   const float inv = 1.0f / L;
   const float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
@@ -734,6 +754,16 @@ static void launch_bf16(const AttnCfg& c, dim3 grid, const AttnArgs& a, hipStrea
   hipLaunchKernelGGL((attn_bf16_kernel<HD, 8, 4, false>), grid, dim3(512), 0, st, a);
 }
 
+template <int HD>
+static void launch_merge(int nsplit, dim3 grid, const AttnArgs& a, hipStream_t st) {
+  switch (nsplit) {
+    case 2: hipLaunchKernelGGL((attn_merge_kernel<HD, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((attn_merge_kernel<HD, 4>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((attn_merge_kernel<HD, 8>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((attn_merge_kernel<HD>), grid, dim3(256), 0, st, a); break;
+  }
+}
+
 // exact pass over the selected rows (plus, when `ctx` carries them, the state outputs)
 static hipError_t launch_exact_bf16(const ProjShape& s, float scale, const void* q_sel,
                                     const void* k_cache, const void* v_cache,
@@ -786,10 +816,8 @@ static hipError_t launch_exact_bf16(const ProjShape& s, float scale, const void*
   if (e != hipSuccess || a.nsplit == 1) return e;
   const size_t threads = (size_t)s.m_cap * s.H * (s.hd / 4);
   dim3 mg((unsigned)((threads + 255) / 256));
-  if (s.hd == 64)
-    hipLaunchKernelGGL(attn_merge_kernel<64>, mg, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_merge_kernel<128>, mg, dim3(256), 0, st, a);
+  if (s.hd == 64) launch_merge<64>(a.nsplit, mg, a, st);
+  else launch_merge<128>(a.nsplit, mg, a, st);
   return hipGetLastError();
 }
 

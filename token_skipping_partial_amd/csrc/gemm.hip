@@ -171,6 +171,69 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const Tin* in, const 
   }
 }
 
+// Row-resident variant (d <= CH * 2048): thread t owns 8-element chunks t, t + 256, ...; the row
+// is loaded once (all loads issued together) and normalised from registers. Same sums in the same
+// order as the kernel above.
+template <typename Tin, typename Tout, int CH>
+__global__ __launch_bounds__(256) void rmsnorm_rows_reg_kernel(const Tin* in, const int32_t* sel_idx,
+                                                               const Tout* g, Tout* out, int d,
+                                                               float eps, const int32_t* row_ptr,
+                                                               int B, int m_cap) {
+  const int j = blockIdx.x;
+  if (j >= live_rows(row_ptr, B, m_cap)) return;
+  const size_t row = sel_idx ? (size_t)sel_idx[j] : (size_t)j;
+  const Tin* x = in + row * d;
+  __shared__ float red[4];
+  float v[CH][8];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = 8 * (threadIdx.x + 256 * c);
+    if (i < d) Elem<Tin>::load8(x + i, v[c]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+    if (8 * (threadIdx.x + 256 * c) < d) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[c][e], v[c][e], ss);
+    }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float r = 1.0f / sqrtf(tot / (float)d + eps);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = 8 * (threadIdx.x + 256 * c);
+    if (i < d) {
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        float gv[4];
+        Elem<Tout>::load4(g + i + 4 * hlf, gv);
+        const float o[4] = {v[c][4 * hlf] * r * gv[0], v[c][4 * hlf + 1] * r * gv[1],
+                            v[c][4 * hlf + 2] * r * gv[2], v[c][4 * hlf + 3] * r * gv[3]};
+        Elem<Tout>::store4(out + (size_t)j * d + i + 4 * hlf, o);
+      }
+    }
+  }
+}
+
+// gather + RMSNorm of the selected rows (row-resident kernel up to d = 8192)
+template <typename Tin, typename Tout>
+static void launch_rmsnorm_rows(const Tin* in, const int32_t* sel_idx, const Tout* g, Tout* out,
+                                int d, float eps, const int32_t* row_ptr, int B, int m_cap,
+                                hipStream_t st) {
+  const dim3 grid(m_cap), blk(256);
+  if (d % 8 == 0 && d <= 2048)
+    hipLaunchKernelGGL((rmsnorm_rows_reg_kernel<Tin, Tout, 1>), grid, blk, 0, st, in, sel_idx, g, out, d, eps, row_ptr, B, m_cap);
+  else if (d % 8 == 0 && d <= 4096)
+    hipLaunchKernelGGL((rmsnorm_rows_reg_kernel<Tin, Tout, 2>), grid, blk, 0, st, in, sel_idx, g, out, d, eps, row_ptr, B, m_cap);
+  else if (d % 8 == 0 && d <= 8192)
+    hipLaunchKernelGGL((rmsnorm_rows_reg_kernel<Tin, Tout, 4>), grid, blk, 0, st, in, sel_idx, g, out, d, eps, row_ptr, B, m_cap);
+  else
+    hipLaunchKernelGGL((rmsnorm_rows_kernel<Tin, Tout>), grid, blk, 0, st, in, sel_idx, g, out, d, eps, row_ptr, B, m_cap);
+}
+
 // =========================================================================================
 // bf16 matrix-core GEMM fed by a direct-to-LDS load ring
 // =========================================================================================
@@ -187,7 +250,6 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const Tin* in, const 
 // the 12288 rows; gate/up: 48 + 48 rows); 4 waves split the M rows, so every X row is read from
 // LDS once. Narrow N (4096) uses BN = 64 and a few K splits. At larger M, 128 x 128 tiles with
 // 2 x 2 waves.
-constexpr int kBK = 64;
 
 // Tiles of the 32 x 32 x 16 kernel used when more than 128 rows are selected (measured on MI355X
 // at the LLaDA-8B shapes): 256 x 256 tiles for many rows (8192), 128 x 256 for a few thousand
@@ -631,8 +693,9 @@ __global__ __launch_bounds__(256) void splitk_swiglu_kernel(const float* partial
   epi(epi.row(m), n, gv, uv);
 }
 
-// fixed-order sum of the K-split partials, then the epilogue
-template <class Epi>
+// fixed-order sum of the K-split partials, then the epilogue. SPLITS > 0: that many partials,
+// all loaded before the sum; SPLITS == 0: `splits` of them, one after the other.
+template <class Epi, int SPLITS = 0>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* partial, int splits,
                                                             int N, const int32_t* row_ptr, int B,
                                                             int m_cap, Epi epi) {
@@ -643,10 +706,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* partial
   if (m >= M) return;
   const int n = (int)(idx - (size_t)m * groups) * 4;
   float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int z = 0; z < splits; ++z) {
-    float p[4];
-    Elem<float>::load4(partial + ((size_t)z * m_cap + m) * N + n, p);
-    v[0] += p[0]; v[1] += p[1]; v[2] += p[2]; v[3] += p[3];
+  if constexpr (SPLITS > 0) {
+    float p[SPLITS][4];
+#pragma unroll
+    for (int z = 0; z < SPLITS; ++z) Elem<float>::load4(partial + ((size_t)z * m_cap + m) * N + n, p[z]);
+#pragma unroll
+    for (int z = 0; z < SPLITS; ++z) {
+      v[0] += p[z][0]; v[1] += p[z][1]; v[2] += p[z][2]; v[3] += p[z][3];
+    }
+  } else {
+    for (int z = 0; z < splits; ++z) {
+      float p[4];
+      Elem<float>::load4(partial + ((size_t)z * m_cap + m) * N + n, p);
+      v[0] += p[0]; v[1] += p[1]; v[2] += p[2]; v[3] += p[3];
+    }
   }
   epi(epi.row(m), n, v);
 }
@@ -861,9 +934,17 @@ static hipError_t run_gemm_bf16(const GemmPlan& p, const uint16_t* X, const uint
   if constexpr (SWIGLU)
     hipLaunchKernelGGL((splitk_swiglu_kernel<Epi>), dim3((unsigned)((groups + 255) / 256)),
                        dim3(256), 0, st, partial, p.splits, N, row_ptr, B, m_cap, epi);
-  else
-    hipLaunchKernelGGL((splitk_reduce_kernel<Epi>), dim3((unsigned)((groups + 255) / 256)),
-                       dim3(256), 0, st, partial, p.splits, N, row_ptr, B, m_cap, epi);
+  else {
+    const dim3 rg((unsigned)((groups + 255) / 256)), rb(256);
+    if (p.splits == 2)
+      hipLaunchKernelGGL((splitk_reduce_kernel<Epi, 2>), rg, rb, 0, st, partial, 2, N, row_ptr, B, m_cap, epi);
+    else if (p.splits == 4)
+      hipLaunchKernelGGL((splitk_reduce_kernel<Epi, 4>), rg, rb, 0, st, partial, 4, N, row_ptr, B, m_cap, epi);
+    else if (p.splits == 8)
+      hipLaunchKernelGGL((splitk_reduce_kernel<Epi, 8>), rg, rb, 0, st, partial, 8, N, row_ptr, B, m_cap, epi);
+    else
+      hipLaunchKernelGGL((splitk_reduce_kernel<Epi>), rg, rb, 0, st, partial, p.splits, N, row_ptr, B, m_cap, epi);
+  }
   return hipGetLastError();
 }
 
@@ -885,8 +966,7 @@ static hipError_t qkv_impl(const ProjShape& s, const T* h_in, const T* g_attn, c
   const int Nq = s.H * s.hd, Nkv = s.Hkv * s.hd, N = Nq + 2 * Nkv;
   T* xn = reinterpret_cast<T*>(ws);
   float* partial = reinterpret_cast<float*>(ws + align256((size_t)s.m_cap * s.d * sizeof(T)));
-  hipLaunchKernelGGL((rmsnorm_rows_kernel<T, T>), dim3(s.m_cap), dim3(256), 0, st, h_in, sel_idx,
-                     g_attn, xn, s.d, s.eps, row_ptr, s.B, s.m_cap);
+  launch_rmsnorm_rows<T, T>(h_in, sel_idx, g_attn, xn, s.d, s.eps, row_ptr, s.B, s.m_cap, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int hd_log2 = 0;
@@ -939,6 +1019,91 @@ __global__ __launch_bounds__(256) void resid_rmsnorm_kernel(const T* x, const in
   }
 }
 
+// Row-resident variant for d <= 8192: thread t owns 4-element chunks t, t + 256, ... (CH of
+// them) of the row, issues every load of the row (x and each split's partial) before using any,
+// keeps the sums in registers, and writes h and hn from them (no second pass over memory).
+template <typename T, int CH, int SPLITS>
+__global__ __launch_bounds__(256) void resid_rmsnorm_reg_kernel(const T* x, const int32_t* sel_idx,
+                                                                const float* partial,
+                                                                const T* g, float* h, T* hn, int d,
+                                                                float eps, const int32_t* row_ptr,
+                                                                int B, int m_cap) {
+  const int j = blockIdx.x;
+  if (j >= live_rows(row_ptr, B, m_cap)) return;
+  const T* xr = x + (size_t)sel_idx[j] * d;
+  const int nch = d / 4;
+  float v[CH][4], p[SPLITS][CH][4];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = 4 * (threadIdx.x + 256 * c);
+    if (i < d) {
+      Elem<T>::load4(xr + i, v[c]);
+#pragma unroll
+      for (int z = 0; z < SPLITS; ++z)
+        Elem<float>::load4(partial + ((size_t)z * m_cap + j) * d + i, p[z][c]);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    if (threadIdx.x + 256 * c < nch) {
+#pragma unroll
+      for (int z = 0; z < SPLITS; ++z)  // fixed order, as the generic kernel
+        for (int e = 0; e < 4; ++e) v[c][e] += p[z][c][e];
+      Elem<float>::store4(h + (size_t)j * d + 4 * (threadIdx.x + 256 * c), v[c]);
+      ss = fmaf(v[c][0], v[c][0], fmaf(v[c][1], v[c][1], fmaf(v[c][2], v[c][2], fmaf(v[c][3], v[c][3], ss))));
+    }
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = 4 * (threadIdx.x + 256 * c);
+    if (i < d) {
+      float gv[4];
+      Elem<T>::load4(g + i, gv);
+      const float o[4] = {v[c][0] * r * gv[0], v[c][1] * r * gv[1], v[c][2] * r * gv[2],
+                          v[c][3] * r * gv[3]};
+      Elem<T>::store4(hn + (size_t)j * d + i, o);
+    }
+  }
+}
+
+template <typename T, int CH>
+static bool launch_resid_rmsnorm_reg(int splits, dim3 grid, hipStream_t st, const T* x,
+                                     const int32_t* sel, const float* partial, const T* g,
+                                     float* h, T* hn, int d, float eps, const int32_t* rp, int B,
+                                     int m_cap) {
+  switch (splits) {
+    case 2: hipLaunchKernelGGL((resid_rmsnorm_reg_kernel<T, CH, 2>), grid, dim3(256), 0, st, x, sel, partial, g, h, hn, d, eps, rp, B, m_cap); return true;
+    case 4: hipLaunchKernelGGL((resid_rmsnorm_reg_kernel<T, CH, 4>), grid, dim3(256), 0, st, x, sel, partial, g, h, hn, d, eps, rp, B, m_cap); return true;
+    case 8: hipLaunchKernelGGL((resid_rmsnorm_reg_kernel<T, CH, 8>), grid, dim3(256), 0, st, x, sel, partial, g, h, hn, d, eps, rp, B, m_cap); return true;
+    default: return false;
+  }
+}
+
+// h = h_in[sel] + sum of the K-split partials, hn = RMSNorm(h) * g: the row-resident kernel when
+// the width and split count allow, else the generic one
+template <typename T>
+static void launch_resid_rmsnorm(const ProjShape& s, int splits, const T* h_in,
+                                 const int32_t* sel_idx, const float* partial, const T* g,
+                                 float* h, T* hn, const int32_t* row_ptr, hipStream_t st) {
+  const dim3 grid(s.m_cap);
+  const int ch = (s.d + 1023) / 1024;
+  bool done = false;
+  if (s.d % 4 == 0) {
+    if (ch <= 1) done = launch_resid_rmsnorm_reg<T, 1>(splits, grid, st, h_in, sel_idx, partial, g, h, hn, s.d, s.eps, row_ptr, s.B, s.m_cap);
+    else if (ch <= 2) done = launch_resid_rmsnorm_reg<T, 2>(splits, grid, st, h_in, sel_idx, partial, g, h, hn, s.d, s.eps, row_ptr, s.B, s.m_cap);
+    else if (ch <= 4) done = launch_resid_rmsnorm_reg<T, 4>(splits, grid, st, h_in, sel_idx, partial, g, h, hn, s.d, s.eps, row_ptr, s.B, s.m_cap);
+  }
+  if (!done)
+    hipLaunchKernelGGL((resid_rmsnorm_kernel<T>), grid, dim3(256), 0, st, h_in, sel_idx, partial,
+                       splits, g, h, hn, s.d, s.eps, row_ptr, s.B, s.m_cap);
+}
+
 template <typename T>
 static hipError_t ffn_impl(const ProjShape& s, const T* h_in, const T* o_sel, const T* w_o,
                            const T* g_ffn, const T* w_gate, const T* w_up, const T* w_down,
@@ -964,17 +1129,14 @@ static hipError_t ffn_impl(const ProjShape& s, const T* h_in, const T* o_sel, co
                              e1, st, /*reduce=*/false);
     if (e != hipSuccess) return e;
     if (po.splits > 1)
-      hipLaunchKernelGGL((resid_rmsnorm_kernel<T>), dim3(s.m_cap), dim3(256), 0, st, h_in,
-                         sel_idx, partial, po.splits, g_ffn, hbuf, hn, s.d, s.eps, row_ptr, s.B,
-                         s.m_cap);
+      launch_resid_rmsnorm<T>(s, po.splits, h_in, sel_idx, partial, g_ffn, hbuf, hn, row_ptr, st);
     else
-      hipLaunchKernelGGL((rmsnorm_rows_kernel<float, T>), dim3(s.m_cap), dim3(256), 0, st, hbuf,
-                         nullptr, g_ffn, hn, s.d, s.eps, row_ptr, s.B, s.m_cap);
+      launch_rmsnorm_rows<float, T>(hbuf, nullptr, g_ffn, hn, s.d, s.eps, row_ptr, s.B, s.m_cap,
+                                    st);
   } else {
     e = run_gemm_f32<false>(o_sel, w_o, nullptr, s.d, Nq, row_ptr, s.B, s.m_cap, e1, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((rmsnorm_rows_kernel<float, T>), dim3(s.m_cap), dim3(256), 0, st, hbuf,
-                       nullptr, g_ffn, hn, s.d, s.eps, row_ptr, s.B, s.m_cap);
+    launch_rmsnorm_rows<float, T>(hbuf, nullptr, g_ffn, hn, s.d, s.eps, row_ptr, s.B, s.m_cap, st);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
