@@ -80,13 +80,20 @@ typedef enum {
  *   B batch rows (sequences), S positions per sequence, d model width, H query heads,
  *   Hkv key/value heads (H % Hkv == 0; query head h reads kv head h / (H / Hkv)), hd head width,
  *   F FFN inner width, dtype a dllm_dtype, V vocabulary size (saliency only), rms_eps RMSNorm
- *   epsilon. */
+ *   epsilon.
+ *   m_plan (>= 0): number of selected rows the layer calls tune their launch plans for (tile
+ *   shapes, K and key splits); 0 means m_cap. With threshold selection M is only known on the
+ *   device, and m_cap must cover the worst case; m_plan lets a caller that expects far fewer rows
+ *   (for example last step's count) get the plan for those. Every M <= m_cap is still computed
+ *   in full whatever m_plan says; only the speed and, through the split points of float32
+ *   sums, the rounding of the results depend on it. The workspace size depends on it too
+ *   (query dllm_workspace_bytes with the same shape). */
 typedef struct {
   int32_t B, S, d, H, Hkv, hd, F;
   int32_t dtype;
   int64_t V;
   float rms_eps;
-  int32_t reserved; /* must be 0 */
+  int32_t m_plan;
 } dllm_shape;
 
 #define DLLM_MAX_SELECT_S 8192 /* largest S dllm_select_compact accepts (one row lives in LDS) */
@@ -221,7 +228,9 @@ dllm_status dllm_gather_rows(const dllm_shape* shape, const void* src, int32_t w
                              void* dst, void* stream);
 
 /* Bytes of device workspace the call `op` (a dllm_op) needs for this shape and m_cap; 0 when
- * none. Returns (size_t)-1 for an invalid op or shape. Pure host function. */
+ * none. With shape->m_plan == 0 the size is that of the plan for m_cap rows; with m_plan > 0 it
+ * covers every m_plan in [1, m_cap], so a caller may change m_plan from call to call without
+ * reallocating. Returns (size_t)-1 for an invalid op or shape. Pure host function. */
 size_t dllm_workspace_bytes(int32_t op, const dllm_shape* shape, int32_t m_cap);
 
 /* Static, NUL-terminated name of a dllm_status value. */

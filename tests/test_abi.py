@@ -41,6 +41,7 @@ def test_library_exports_every_declared_symbol():
 def test_shape_struct_layout():
     assert ctypes.sizeof(tsp.Shape) == 48
     assert tsp.Shape.V.offset == 32 and tsp.Shape.rms_eps.offset == 40
+    assert tsp.Shape.m_plan.offset == 44
 
 
 def test_status_strings_and_version():
@@ -67,6 +68,20 @@ def test_workspace_sizes():
         tsp.dllm_workspace_bytes(7, s, 128)
     with pytest.raises(tsp.DllmError):
         tsp.dllm_workspace_bytes(tsp.OP_QKV, s, 1025)  # m_cap > B*S
+
+
+def test_workspace_covers_every_planned_row_count():
+    """With m_plan > 0 the size does not depend on m_plan and covers the m_cap plan, so a caller
+    may change m_plan between calls; m_plan above m_cap plans for m_cap."""
+    for s, cap in ((llada(), 1024), (llada(B=8), 1640),
+                   (tsp.Shape(B=16, S=2048, d=3584, H=28, Hkv=4, hd=128, F=18944), 16384),
+                   (tsp.Shape(B=2, S=160, d=256, H=8, Hkv=2, hd=64, F=512), 320)):
+        for op in (tsp.OP_QKV, tsp.OP_ATTN, tsp.OP_FFN):
+            base = tsp.dllm_workspace_bytes(op, s, cap)
+            sizes = {tsp.dllm_workspace_bytes(op, s.with_plan(p), cap)
+                     for p in (1, 2, 64, 65, 100, 128, 129, 200, 256, 257, 300, 1000, cap, 10 * cap)}
+            assert len(sizes) == 1 and sizes.pop() >= base
+            assert tsp.dllm_workspace_bytes(op, s.with_plan(0), cap) == base
 
 
 def rc(fn, *args):
@@ -123,11 +138,11 @@ def test_layer_call_validation():
     assert rc(a, bad, 0.1, P, P, P, P, P, 128, P, ws) == tsp.DLLM_ERR_UNSUPPORTED
     bad = llada(); bad.d = 4000
     assert rc(ff, bad, P, P, P, P, P, P, P, P, P, 128, P, ws) == tsp.DLLM_ERR_UNSUPPORTED
-    # non-finite scale, bad dtype, nonzero reserved field
+    # non-finite scale, bad dtype, negative m_plan
     assert rc(a, s, float("inf"), P, P, P, P, P, 128, P, ws) == tsp.DLLM_ERR_INVALID_ARG
     bad = llada(); bad.dtype = 7
     assert rc(q, bad, P, P, P, P, P, 128, P, P, P, ws) == tsp.DLLM_ERR_INVALID_ARG
-    bad = llada(); bad.reserved = 1
+    bad = llada(); bad.m_plan = -1
     assert rc(q, bad, P, P, P, P, P, 128, P, P, P, ws) == tsp.DLLM_ERR_INVALID_ARG
     # workspace too small (reported before any launch)
     lib = tsp.library()

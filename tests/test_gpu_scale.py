@@ -186,3 +186,63 @@ def test_select_batched_step_size(lib):
     check_select(lib, score, force, O.SEL_TOPK, k=64)
     score = synth.adversarial_scores(16, 2048, seed=53, kind="ties")
     check_select(lib, score, None, O.SEL_TOPK, k=1024)
+
+
+@pytest.mark.parametrize("m_plan", [1, 128, 200, 300, 5000])
+def test_planned_rows_do_not_change_results(lib, m_plan):
+    """LLaDA-8B layer (B=1, S=1024), 200 selected rows, capacity every token, and plans made for
+    1 (64-row tiles, 4 row tiles), 128, 200 (256-row tiles), 300 (32x32 tiles with K splits) and
+    more than the capacity: every selected row is still computed and matches the oracle, and
+    nothing else is written. Each call takes its inputs from the generators."""
+    d = W.LLADA_LAYER
+    print(f"planned rows {m_plan}", flush=True)
+    sel, rp = even_selection(d.B, d.S, 200, 61)
+    M, cap = int(rp[-1]), d.B * d.S
+    w = weights_gpu(d, 930)
+    h_in = synth.normal((d.B, d.S, d.d), 1.0, 931, BF16, "cuda")
+    kc = synth.normal((d.B, d.Hkv, d.S, d.hd), 1.0, 932, BF16, "cuda")
+    vc = synth.normal((d.B, d.Hkv, d.S, d.hd), 1.0, 933, BF16, "cuda")
+    kc0 = kc.clone()
+    q_in = synth.normal((cap, d.H * d.hd), 1.0, 935, BF16, "cuda")
+    o_in = synth.normal((cap, d.H * d.hd), 1.0, 936, BF16, "cuda")
+    h_out = synth.normal((d.B, d.S, d.d), 1.0, 934, BF16, "cuda")
+    h_out0 = h_out.clone()
+    shape = shape_of(lib, d).with_plan(m_plan)
+    sel_d, rp_d = to_dev(sel), to_dev(rp)
+    q = torch.zeros(cap, d.H * d.hd, dtype=BF16, device="cuda")
+    o = torch.zeros(cap, d.H * d.hd, dtype=BF16, device="cuda")
+    scale = 1.0 / math.sqrt(d.hd)
+    lib.dllm_partial_attn(shape, scale, q_in, kc, vc, sel_d, rp_d, cap, o,
+                          lib.workspace(lib.OP_ATTN, shape, cap))
+    lib.dllm_gather_ffn_scatter(shape, h_in, o_in, w["w_o"], w["g_ffn"], w["w_gate"], w["w_up"],
+                                w["w_down"], sel_d, rp_d, cap, h_out,
+                                lib.workspace(lib.OP_FFN, shape, cap))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(M, 62)[:24], [M - 1]]))  # M-1: ragged tile
+    s_sub, rp_sub = subset(sel, rows, d.S, d.B)
+    bs, ss = s_sub // d.S, s_sub % d.S
+    rows_t = torch.from_numpy(rows).cuda()
+    bs_t, ss_t = torch.from_numpy(bs).cuda(), torch.from_numpy(ss).cuda()
+    tol = TOL[BF16]
+    ra = O.partial_attn(host(q_in[rows_t]), host(kc), host(vc), s_sub, rp_sub, d.H, d.Hkv, d.hd,
+                        scale)
+    assert_close(host(o[rows_t]), ra, tol, "o_sel (sampled)")
+    rf = O.gather_ffn_scatter(host(h_in), host(o_in[rows_t]), host(w["w_o"]), host(w["g_ffn"]),
+                              host(w["w_gate"]), host(w["w_up"]), host(w["w_down"]), s_sub, rp_sub,
+                              np.zeros((d.B, d.S, d.d)), 1e-5)
+    assert_close(host(h_out[bs_t, ss_t]), rf[bs, ss], tol, "h_out rows (sampled)")
+    # the projection last: it rewrites the cache rows the attention above read
+    lib.dllm_gather_qkv_scatter_kv(shape, h_in, w["g_attn"], w["w_qkv"], sel_d, rp_d, cap, q, kc,
+                                   vc, lib.workspace(lib.OP_QKV, shape, cap))
+    torch.cuda.synchronize()
+    zeros = np.zeros((d.B, d.Hkv, d.S, d.hd))
+    rq, rk, _ = O.gather_qkv_scatter_kv(host(h_in), host(w["g_attn"]), host(w["w_qkv"]), s_sub,
+                                        rp_sub, zeros, zeros, d.H, d.Hkv, d.hd, 1e-5)
+    assert_close(host(q[rows_t]), rq, tol, "q_sel (sampled)")
+    assert_close(host(kc[bs_t, :, ss_t, :]), rk[bs, :, ss, :], tol, "k_cache rows (sampled)")
+    # rows past M of the compact outputs and unselected cache / hidden rows are untouched
+    assert not q[M:].any() and not o[M:].any()
+    mask = torch.ones(d.B, d.S, dtype=torch.bool, device="cuda")
+    mask[torch.from_numpy(sel // d.S).cuda().long(), torch.from_numpy(sel % d.S).cuda().long()] = False
+    assert same_bits(kc.permute(0, 2, 1, 3)[mask], kc0.permute(0, 2, 1, 3)[mask])
+    assert same_bits(h_out[mask], h_out0[mask])

@@ -39,16 +39,25 @@ class DllmError(RuntimeError):
 
 
 class Shape(ctypes.Structure):
-    """dllm_shape: B, S, d, H, Hkv, hd, F, dtype, V, rms_eps (48 bytes)."""
+    """dllm_shape: B, S, d, H, Hkv, hd, F, dtype, V, rms_eps, m_plan (48 bytes).
+    m_plan: rows the layer calls tune their launch plans for (0 = m_cap); results cover every
+    selected row whatever its value."""
     _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("hd", ctypes.c_int32),
                 ("F", ctypes.c_int32), ("dtype", ctypes.c_int32), ("V", ctypes.c_int64),
-                ("rms_eps", ctypes.c_float), ("reserved", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("m_plan", ctypes.c_int32)]
 
     def __init__(self, B=1, S=1, d=64, H=1, Hkv=1, hd=64, F=64, dtype="bf16", V=0,
-                 rms_eps=1e-5):
+                 rms_eps=1e-5, m_plan=0):
         dt = {"bf16": BF16, "f32": F32, BF16: BF16, F32: F32}[dtype]
-        super().__init__(B, S, d, H, Hkv, hd, F, dt, V, rms_eps, 0)
+        super().__init__(B, S, d, H, Hkv, hd, F, dt, V, rms_eps, m_plan)
+
+    def with_plan(self, m_plan: int) -> "Shape":
+        """A copy of this shape with another m_plan."""
+        s = Shape()
+        ctypes.pointer(s)[0] = self
+        s.m_plan = int(m_plan)
+        return s
 
     @property
     def torch_dtype(self):
@@ -57,7 +66,7 @@ class Shape(ctypes.Structure):
     def __repr__(self):
         return (f"Shape(B={self.B}, S={self.S}, d={self.d}, H={self.H}, Hkv={self.Hkv}, "
                 f"hd={self.hd}, F={self.F}, dtype={'bf16' if self.dtype == BF16 else 'f32'}, "
-                f"V={self.V}, rms_eps={self.rms_eps})")
+                f"V={self.V}, rms_eps={self.rms_eps}, m_plan={self.m_plan})")
 
 
 def _load():

@@ -14,7 +14,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool base_shape_ok(const dllm_shape* s) {
   return s && s->B > 0 && s->S > 0 && s->d > 0 && (s->dtype == DLLM_F32 || s->dtype == DLLM_BF16) &&
-         s->reserved == 0 && (long)s->B * (long)s->S <= 0x7fffffffL;
+         s->m_plan >= 0 && (long)s->B * (long)s->S <= 0x7fffffffL;
 }
 
 // shape checks shared by the three layer calls; INVALID_ARG before UNSUPPORTED
@@ -33,6 +33,7 @@ ProjShape proj_shape(const dllm_shape* s, int32_t m_cap) {
   p.B = s->B; p.S = s->S; p.d = s->d; p.H = s->H; p.Hkv = s->Hkv; p.hd = s->hd; p.F = s->F;
   p.eps = s->rms_eps;
   p.m_cap = m_cap;
+  p.m_plan = (s->m_plan > 0 && s->m_plan < m_cap) ? s->m_plan : m_cap;
   return p;
 }
 
@@ -50,7 +51,7 @@ dllm_status ws_status(const void* ws, size_t have, size_t need) {
 extern "C" {
 
 static_assert(DLLM_MAX_SALIENT_S == kSalientMaxS, "stable-token pass limit");
-int32_t dllm_version(void) { return 101; }
+int32_t dllm_version(void) { return 102; }
 
 const char* dllm_status_string(int32_t status) {
   switch (status) {
@@ -74,10 +75,24 @@ size_t dllm_workspace_bytes(int32_t op, const dllm_shape* shape, int32_t m_cap) 
     case DLLM_OP_FFN: {
       if (layer_shape_status(shape, m_cap) != DLLM_OK) return (size_t)-1;
       const bool bf16 = shape->dtype == DLLM_BF16;
-      const ProjShape p = proj_shape(shape, m_cap);
-      if (op == DLLM_OP_QKV) return qkv_workspace_bytes(bf16, p);
-      if (op == DLLM_OP_ATTN) return attn_workspace_bytes(bf16, p);
-      return ffn_workspace_bytes(bf16, p);
+      ProjShape p = proj_shape(shape, m_cap);
+      auto bytes = [&](const ProjShape& q) {
+        if (op == DLLM_OP_QKV) return qkv_workspace_bytes(bf16, q);
+        if (op == DLLM_OP_ATTN) return attn_workspace_bytes(bf16, q);
+        return ffn_workspace_bytes(bf16, q);
+      };
+      if (shape->m_plan == 0) return bytes(p);
+      // any m_plan: inside a GEMM plan class the K split only shrinks as the planned rows grow,
+      // so the first row count of each class bounds it; the attention key split is largest at
+      // one planned row (its estimate of busy workgroups is smallest there)
+      size_t most = bytes(p);
+      for (int r : {1, 65, 129, kWsMaxRows + 1, kG32BigRows}) {
+        if (r > m_cap) break;
+        p.m_plan = r;
+        const size_t b = bytes(p);
+        if (b > most) most = b;
+      }
+      return most;
     }
     default:
       return (size_t)-1;

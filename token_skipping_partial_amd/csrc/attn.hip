@@ -716,7 +716,7 @@ struct AttnCfg {
 static AttnCfg plan_bf16(const ProjShape& s) {
   AttnCfg c;
   const int G = s.H / s.Hkv;
-  const long rows_avg = (long)cdiv((long)s.m_cap * G, s.B);
+  const long rows_avg = (long)cdiv((long)s.m_plan * G, s.B);
   c.nw = (s.hd == 128 || rows_avg > 160) ? 8 : 4;
 #ifdef DLLM_ATTN_FORCE_NW
   c.nw = DLLM_ATTN_FORCE_NW;

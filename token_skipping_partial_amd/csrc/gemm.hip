@@ -260,7 +260,6 @@ struct G32Shape {
 };
 constexpr G32Shape kG32Big{256, 256, 32, 4, 2, 4};
 constexpr G32Shape kG32Mid{128, 256, 32, 2, 4, 4};
-constexpr int kG32BigRows = 4096;  // selected rows from which the big tile is used
 
 // ring slots that fit in the 160 KB of LDS a workgroup may use, capped at `want`
 constexpr int ring_slots(int bm, int bn, int bk, int want) {
@@ -813,18 +812,23 @@ static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 //   wide output (QKV, N = 12288): 48-row slabs (256 tiles), no split;
 //   narrow output (W_o, W_down, N = 4096): 64-row slabs, 4 K splits;  gate/up: 48 + 48 rows.
 // Wider slabs with more K splits move fewer bytes per CU but pay the partial round trip.
-GemmPlan plan_gemm(bool bf16, int m_cap, int N, int K, bool swiglu) {
+// Up to kWsMaxRows rows the weight-streaming tiles hold every row (256 rows: 8 waves of 32;
+// measured at 160-256 rows of the LLaDA-8B layer: QKV 50 vs 56-60 us, FFN 144-148 vs 156-172 us
+// for 128 x 256 tiles of the 32 x 32 x 16 kernel).
+// `rows`: the number of selected rows the plan is made for (the grid itself always covers
+// m_cap rows, so more rows are still computed, by further row tiles).
+GemmPlan plan_gemm(bool bf16, int rows, int N, int K, bool swiglu) {
   GemmPlan p{64, 64, 64, 4, 1, 4, 1};
   if (!bf16) return p;
-  if (m_cap > 128) {
-    const G32Shape t = m_cap >= kG32BigRows ? kG32Big : kG32Mid;
+  if (rows > kWsMaxRows) {
+    const G32Shape t = rows >= kG32BigRows ? kG32Big : kG32Mid;
     p = GemmPlan{t.bm, t.bn, t.bk, t.wm, t.wn, t.st, 1, 32};
-    const long tiles = (long)cdiv(N, swiglu ? p.bn / 2 : p.bn) * cdiv(m_cap, p.bm);
+    const long tiles = (long)cdiv(N, swiglu ? p.bn / 2 : p.bn) * cdiv(rows, p.bm);
     if (!swiglu)
       while (tiles * p.splits < 256 && K / (p.splits * 2) >= 512 && p.splits < 8) p.splits *= 2;
     return p;
   }
-  const int bm = m_cap <= 64 ? 64 : 128;
+  const int bm = rows <= 64 ? 64 : rows <= 128 ? 128 : 256;
   const int wm = bm / 32;  // waves of 32 rows
   if (swiglu) {
     p = GemmPlan{bm, 96, 64, wm, 1, 0, 1};
@@ -850,16 +854,16 @@ static int kchunk_of(const GemmPlan& p, int K) { return cdiv(cdiv(K, p.splits), 
 size_t qkv_workspace_bytes(bool bf16, const ProjShape& s) {
   const int N = (s.H + 2 * s.Hkv) * s.hd;
   const size_t es = bf16 ? 2 : 4;
-  GemmPlan p = plan_gemm(bf16, s.m_cap, N, s.d, false);
+  GemmPlan p = plan_gemm(bf16, s.m_plan, N, s.d, false);
   return align256((size_t)s.m_cap * s.d * es) + align256(gemm_partials_bytes(p, s.m_cap, N));
 }
 
 size_t ffn_workspace_bytes(bool bf16, const ProjShape& s) {
   const size_t es = bf16 ? 2 : 4;
   const int Nq = s.H * s.hd;
-  GemmPlan po = plan_gemm(bf16, s.m_cap, s.d, Nq, false);
-  GemmPlan pg = plan_gemm(bf16, s.m_cap, s.F, s.d, true);
-  GemmPlan pd = plan_gemm(bf16, s.m_cap, s.d, s.F, false);
+  GemmPlan po = plan_gemm(bf16, s.m_plan, s.d, Nq, false);
+  GemmPlan pg = plan_gemm(bf16, s.m_plan, s.F, s.d, true);
+  GemmPlan pd = plan_gemm(bf16, s.m_plan, s.d, s.F, false);
   size_t part = gemm_partials_bytes(po, s.m_cap, s.d);
   const size_t part_g = gemm_partials_bytes(pg, s.m_cap, 2 * s.F);
   const size_t part_d = gemm_partials_bytes(pd, s.m_cap, s.d);
@@ -914,6 +918,7 @@ static hipError_t run_gemm_bf16(const GemmPlan& p, const uint16_t* X, const uint
              p, g, grid, epi, st) ||
          launch32_if<kG32Mid.bm, kG32Mid.bn, kG32Mid.bk, kG32Mid.wm, kG32Mid.wn, kG32Mid.st, true>(
              p, g, grid, epi, st) ||
+         launch_if<256, 96, 64, 8, 1, RS(256, 96), true>(p, g, grid, epi, st) ||
          launch_if<128, 96, 64, 4, 1, RS(128, 96), true>(p, g, grid, epi, st) ||
          launch_if<64, 96, 64, 2, 1, RS(64, 96), true>(p, g, grid, epi, st);
   } else {
@@ -921,6 +926,8 @@ static hipError_t run_gemm_bf16(const GemmPlan& p, const uint16_t* X, const uint
              p, g, grid, epi, st) ||
          launch32_if<kG32Mid.bm, kG32Mid.bn, kG32Mid.bk, kG32Mid.wm, kG32Mid.wn, kG32Mid.st, false>(
              p, g, grid, epi, st) ||
+         launch_if<256, 48, 64, 8, 1, RS(256, 48), false>(p, g, grid, epi, st) ||
+         launch_if<256, 64, 64, 8, 1, RS(256, 64), false>(p, g, grid, epi, st) ||
          launch_if<128, 48, 64, 4, 1, RS(128, 48), false>(p, g, grid, epi, st) ||
          launch_if<128, 64, 64, 4, 1, RS(128, 64), false>(p, g, grid, epi, st) ||
          launch_if<64, 48, 64, 2, 1, RS(64, 48), false>(p, g, grid, epi, st) ||
@@ -973,7 +980,7 @@ static hipError_t qkv_impl(const ProjShape& s, const T* h_in, const T* g_attn, c
   while ((1 << hd_log2) < s.hd) ++hd_log2;  // hd is 64 or 128
   EpiQKV<T> epi{q_sel, kc, vc, sel_idx, Nq, Nkv, hd_log2, s.S, s.Hkv, FastDiv::make((uint32_t)s.S)};
   if constexpr (kBf16) {
-    GemmPlan p = plan_gemm(true, s.m_cap, N, s.d, false);
+    GemmPlan p = plan_gemm(true, s.m_plan, N, s.d, false);
     return run_gemm_bf16<false>(p, xn, w_qkv, nullptr, N, s.d, row_ptr, s.B, s.m_cap, partial,
                                 epi, st);
   } else {
@@ -1124,7 +1131,7 @@ static hipError_t ffn_impl(const ProjShape& s, const T* h_in, const T* o_sel, co
   // h = h_in[sel] + o_sel W_o^T ; hn = RMSNorm(h) * g_ffn
   EpiResidF32<T> e1{hbuf, h_in, sel_idx, s.d};
   if constexpr (kBf16) {
-    const GemmPlan po = plan_gemm(true, s.m_cap, s.d, Nq, false);
+    const GemmPlan po = plan_gemm(true, s.m_plan, s.d, Nq, false);
     e = run_gemm_bf16<false>(po, o_sel, w_o, nullptr, s.d, Nq, row_ptr, s.B, s.m_cap, partial,
                              e1, st, /*reduce=*/false);
     if (e != hipSuccess) return e;
@@ -1143,7 +1150,7 @@ static hipError_t ffn_impl(const ProjShape& s, const T* h_in, const T* o_sel, co
   // z = silu(hn W_gate^T) * (hn W_up^T)
   EpiSwiGLU<T> e2{z, s.F};
   if constexpr (kBf16)
-    e = run_gemm_bf16<true>(plan_gemm(true, s.m_cap, s.F, s.d, true), hn, w_gate, w_up, s.F, s.d,
+    e = run_gemm_bf16<true>(plan_gemm(true, s.m_plan, s.F, s.d, true), hn, w_gate, w_up, s.F, s.d,
                             row_ptr, s.B, s.m_cap, partial, e2, st);
   else
     e = run_gemm_f32<true>(hn, w_gate, w_up, s.F, s.d, row_ptr, s.B, s.m_cap, e2, st);
@@ -1152,7 +1159,7 @@ static hipError_t ffn_impl(const ProjShape& s, const T* h_in, const T* o_sel, co
   // h_out[sel] = h + z W_down^T
   EpiResidScatter<T> e3{h_out, hbuf, sel_idx, s.d};
   if constexpr (kBf16)
-    e = run_gemm_bf16<false>(plan_gemm(true, s.m_cap, s.d, s.F, false), z, w_down, nullptr, s.d,
+    e = run_gemm_bf16<false>(plan_gemm(true, s.m_plan, s.d, s.F, false), z, w_down, nullptr, s.d,
                              s.F, row_ptr, s.B, s.m_cap, partial, e3, st);
   else
     e = run_gemm_f32<false>(z, w_down, nullptr, s.d, s.F, row_ptr, s.B, s.m_cap, e3, st);

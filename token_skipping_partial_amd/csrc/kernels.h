@@ -36,11 +36,20 @@ struct ProjShape {
   int B, S, d, H, Hkv, hd, F;
   float eps;
   int m_cap;
+  int m_plan;  // rows the launch plans are tuned for (1 <= m_plan <= m_cap, or 0 when m_cap is 0)
 };
+
+// GEMM plan classes by planned rows: weight-streaming tiles that hold every row up to
+// kWsMaxRows (64 / 128 / 256-row tiles), then 32 x 32 x 16 tiles, the big ones from kG32BigRows.
+#ifndef DLLM_WS_MAX_ROWS
+#define DLLM_WS_MAX_ROWS 256
+#endif
+constexpr int kWsMaxRows = DLLM_WS_MAX_ROWS;
+constexpr int kG32BigRows = 4096;
 
 // launch plan of one GEMM: tile height, number of K splits
 struct GemmPlan {
-  int bm;      // rows of X per tile (bf16: 64 or 128); the fp32 path uses 64 x 64 tiles
+  int bm;      // rows of X per tile (bf16: 64, 128 or 256); the fp32 path uses 64 x 64 tiles
   int bn;      // weight rows per tile (SwiGLU: gate + up rows)
   int bk;      // K columns per LDS ring slot (64 or 128)
   int wm, wn;  // wave grid
@@ -49,7 +58,7 @@ struct GemmPlan {
   int mfma = 16;  // matrix-core block edge: 16 (16x16x32) or 32 (32x32x16)
 };
 // N = output columns (SwiGLU: F, the tile then holds gate and up rows of the same columns)
-GemmPlan plan_gemm(bool bf16, int m_cap, int N, int K, bool swiglu);
+GemmPlan plan_gemm(bool bf16, int rows, int N, int K, bool swiglu);
 size_t gemm_partials_bytes(const GemmPlan& p, int m_cap, int N);
 
 size_t qkv_workspace_bytes(bool bf16, const ProjShape& s);

@@ -12,6 +12,7 @@ tokens whose FFN is recomputed; those tokens' changed outputs decide the next la
 """
 from __future__ import annotations
 
+import contextlib
 import math
 from dataclasses import dataclass, field
 
@@ -179,6 +180,9 @@ class LayerAdaptiveModel:
       row of hidden[l + 1]; the others keep last step's row. A_{l+1} is that set. A_0 is chosen
       by the L1-normalised change of the layer-0 input against step t-1 (threshold `tau_in`).
     Buffers are sized for every token (the thresholded counts are only known on the device).
+    The calls are told how many rows to plan for (`m_plan`): each row set's count of the last
+    step whose counts have reached the host, with a 1/8 margin. Counts come back by an
+    asynchronous copy, so no step waits for the device; a wrong guess costs speed, never rows.
     """
 
     def __init__(self, shape: Shape, layers: list, tau_in: float, tau_ctx, scale=None,
@@ -204,7 +208,14 @@ class LayerAdaptiveModel:
         self.cur = 0                                  # index of the step-t context buffer
         self.ctx_shape = Shape(B=B, S=S, d=nq, H=H, Hkv=Hkv, hd=hd, F=shape.F,
                                dtype=shape.dtype, V=0)
-        self.scratch = LayerScratch(shape, ntok, device)
+        # workspaces sized for any m_plan (a nonzero m_plan in the shape asks for that size)
+        self.scratch = LayerScratch(shape.with_plan(1), ntok, device)
+        self.plan = [0] * (L + 1)                      # m_plan per row set (0: every token)
+        self._shapes = {}
+        self._counts = torch.zeros(L + 1, dtype=torch.int32, device=device)
+        self._counts_host = torch.zeros(L + 1, dtype=torch.int32,
+                                        pin_memory=torch.device(device).type == "cuda")
+        self._counts_evt = None
         self.k_old = z(ntok, Hkv * hd)
         self.v_old = z(ntok, Hkv * hd)
         self.o_rows = z(ntok, nq)
@@ -215,8 +226,16 @@ class LayerAdaptiveModel:
         self.all_sel, self.all_rp = all_rows(shape, device)
         self.layer_scores = None  # per-layer copies of the context scores (step(record=True))
 
+    def _planned(self, m_plan):
+        sh = self._shapes.get(m_plan)
+        if sh is None:
+            sh = self._shapes[m_plan] = self.shape.with_plan(m_plan)
+        return sh
+
     def _layer(self, l, sel_a, rp_a, sel_f, rp_f, tau, stream):
-        sh, w, sc, n = self.shape, self.layers[l], self.scratch, self.shape.B * self.shape.S
+        w, sc, n = self.layers[l], self.scratch, self.shape.B * self.shape.S
+        sh = self._planned(self.plan[l])       # rows of set l: projection and attention
+        sh_f = self._planned(self.plan[l + 1])  # rows of set l + 1: output projection and FFN
         cur, prev = self.ctx[l][self.cur], self.ctx[l][1 - self.cur]
         dllm_gather_kv_rows(sh, self.k[l], self.v[l], sel_a, rp_a, n, self.k_old, self.v_old,
                             stream)
@@ -237,12 +256,14 @@ class LayerAdaptiveModel:
                                 stream=stream)
         dllm_gather_rows(self.ctx_shape, cur, self.ctx_shape.d, sel_f, rp_f, n, self.o_rows,
                          stream)
-        dllm_gather_ffn_scatter(sh, self.hidden[l], self.o_rows, w.w_o, w.g_ffn, w.w_gate,
+        dllm_gather_ffn_scatter(sh_f, self.hidden[l], self.o_rows, w.w_o, w.g_ffn, w.w_gate,
                                 w.w_up, w.w_down, sel_f, rp_f, n, self.hidden[l + 1], sc.ws_ffn,
                                 stream)
 
     def fill(self, x0, stream=None):
         """Step 0: every layer on every token; primes caches, states and both context buffers."""
+        self.plan = [0] * len(self.plan)
+        self._counts_evt = None
         self.hidden[0].copy_(x0)
         self.x_ref.copy_(x0)
         for l in range(len(self.layers)):
@@ -260,6 +281,9 @@ class LayerAdaptiveModel:
         elif not record:
             self.layer_scores = None
         self.cur = 1 - self.cur
+        if self._counts_evt is not None and self._counts_evt.query():
+            self.plan = [c + c // 8 + 1 for c in self._counts_host.tolist()]
+            self._counts_evt = None
         self.hidden[0].copy_(x)
         dllm_saliency(self.shape, DELTA_L1N, 0.0, self.hidden[0], self.x_ref, None, self.score,
                       stream=stream)
@@ -269,4 +293,11 @@ class LayerAdaptiveModel:
         for l in range(len(self.layers)):
             self._layer(l, self.sel[l], self.rp[l], self.sel[l + 1], self.rp[l + 1], taus[l],
                         stream)
+        if self._counts_evt is None:   # the previous copy has been read: send this step's counts
+            B = self.shape.B
+            with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+                torch.stack([r[B] for r in self.rp], out=self._counts)
+                self._counts_host.copy_(self._counts, non_blocking=True)
+                self._counts_evt = torch.cuda.Event()
+                self._counts_evt.record()
         return self.sel, self.rp
