@@ -40,13 +40,18 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llada_layer",
-                   choices=["llada_layer", "llada_step", "llada_context", "llada_adaptive"],
+                   choices=["llada_layer", "llada_step", "llada_context", "llada_adaptive",
+                            "llada_response"],
                    help="llada_layer: one LLaDA-8B-shaped layer, B=1 (default); llada_step: the "
                         "full 32-layer early-skip step, B=8, S=1024, top-205 per sequence; "
                         "llada_context: the llada_layer step keeping the attention context of "
                         "every token (exact rows for the selected, changed-key update for the rest); "
                         "llada_adaptive: 32 LLaDA-8B layers, B=1, S=1024, per-layer FFN rows chosen "
-                        "by the cosine change of every token's attention context")
+                        "by the cosine change of every token's attention context; "
+                        "llada_response: llada_adaptive with a 512-token prompt left out of "
+                        "response-only steps and re-injected every --inject-every steps")
+    p.add_argument("--inject-every", type=int, default=8,
+                   help="llada_response: every n-th step re-injects the prompt")
     p.add_argument("--sets", type=int, default=16, help="rotated input/weight sets")
     p.add_argument("--context-seq", type=int, default=1024, choices=[1024, 4096],
                    help="llada_context: sequence length (1024: top-128 of the llada_layer "
@@ -107,8 +112,8 @@ def main():
     if args.workload == "llada_context":
         run_llada_context(args)
         return
-    if args.workload == "llada_adaptive":
-        run_llada_adaptive(args)
+    if args.workload in ("llada_adaptive", "llada_response"):
+        run_llada_adaptive(args, response=args.workload == "llada_response")
         return
 
     import token_skipping_partial_amd as tsp  # raises if libdllm.so is not built
@@ -447,13 +452,17 @@ def run_llada_context(args):
     print(json.dumps(out), flush=True)
 
 
-def run_llada_adaptive(args):
+def run_llada_adaptive(args, response=False):
     """32 LLaDA-8B layers, B=1, S=1024, layer-adaptive (DyLLM §2.A/§2.B): the 154 tokens whose
     layer-0 input moved (L1-normalised change > 0.05) are the first layer's rows; in every layer
     the contexts of all tokens are kept and the tokens whose context moved most (cosine change
     above a per-layer threshold, set from an untimed calibration step at the 80th percentile of
     that layer's scores) get W_o + FFN and become the next layer's rows. Inputs cumulative as in
-    llada_step."""
+    llada_step.
+    response=True (DyLLM §2.C): positions 0-511 are the prompt (512 prompt + 512 generation);
+    the 154 moving tokens are drawn among the generation positions, response-only steps leave
+    the prompt out, every --inject-every-th step re-injects it; thresholds from the response
+    positions' scores."""
     import synth
     import token_skipping_partial_amd as tsp
     from synth import workloads as W
@@ -467,11 +476,16 @@ def run_llada_adaptive(args):
     layers = [LayerWeights.from_dict(synth.layer_weights(dims.d, dims.H, dims.Hkv, dims.hd, dims.F,
                                                          seed=7000 + l, device="cuda"))
               for l in range(L)]
-    model = LayerAdaptiveModel(shape, layers, 0.05, [0.0] * L)
+    P = dims.S // 2 if response else 0
+    inject = args.inject_every if response else 0
+    model = LayerAdaptiveModel(shape, layers, 0.05, [0.0] * L, prompt_len=P, inject_every=inject)
     nsteps = args.warmup + args.steps + 1
     xs = [synth.normal((dims.B, dims.S, dims.d), 1.0, 7500, torch.bfloat16, "cuda")]
+    prompt = torch.zeros(dims.B, dims.S, dtype=torch.bool)
+    prompt[:, :P] = True
     for t in range(1, nsteps + 1):
-        large = synth.large_positions(dims.B, dims.S, W.LLADA_LARGE, seed=7600 + t, device="cuda")
+        large = synth.large_positions(dims.B, dims.S, W.LLADA_LARGE, seed=7600 + t,
+                                      exclude=prompt if P else None, device="cuda")
         xs.append(synth.perturb(xs[-1], large, seed=7700 + t))
     model.fill(xs[0])
     # calibration (untimed): context thresholds at the 80th percentile of each layer's scores
@@ -479,7 +493,7 @@ def run_llada_adaptive(args):
     model.layer_scores = None
     for l in range(L):
         model.step(xs[1], tau_ctx=taus + [-1.0] * (L - l), record=True)
-        taus.append(float(torch.quantile(model.layer_scores[l].flatten(), 0.8).item()))
+        taus.append(float(torch.quantile(model.layer_scores[l][:, P:].flatten(), 0.8).item()))
         model.fill(xs[0])
     model.tau_ctx = taus
     for t in range(args.warmup):
@@ -487,14 +501,19 @@ def run_llada_adaptive(args):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    counts = []
+    counts, kinds = [], []
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0.record(stream)
+    evs[0].record(stream)
     for t in range(args.steps):
         sel, rp = model.step(xs[1 + args.warmup + t])
+        evs[t + 1].record(stream)
+        kinds.append(bool(inject) and model.t % inject == 0)
         counts.append(torch.stack([r[-1] for r in rp]))
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    per = [evs[t].elapsed_time(evs[t + 1]) for t in range(args.steps)]
     c = torch.stack(counts).float().mean(0).cpu().tolist()   # [input rows, FFN rows per layer]
     ffn_rows = sum(c[1:])
     qkv_rows = sum(c[:-1])
@@ -512,6 +531,16 @@ def run_llada_adaptive(args):
                    "projection_rows_per_step": round(qkv_rows, 1),
                    "rows_per_layer": [round(v, 1) for v in c]},
     }
+    if response:
+        out["config"]["workload"] = (
+            f"llada_response: llada_adaptive with positions 0-{P - 1} a prompt, left out of "
+            f"response-only steps, re-injected every {inject}th step; 154 moving tokens among "
+            f"the generation positions")
+        ri = [p for p, k in zip(per, kinds) if not k]
+        ij = [p for p, k in zip(per, kinds) if k]
+        out["config"]["ms_response_only_step"] = round(sum(ri) / max(1, len(ri)), 3)
+        out["config"]["ms_inject_step"] = round(sum(ij) / max(1, len(ij)), 3) if ij else None
+        out["config"]["inject_steps_timed"] = len(ij)
     print(json.dumps(out), flush=True)
 
 

@@ -114,14 +114,17 @@ dllm_status dllm_saliency(const dllm_shape* shape, int32_t delta_kind, float alp
                           const void* h_cur, const void* h_prev, const void* logits,
                           float* score, float* conf_out, float* delta_out, void* stream);
 
-/* (2) Selection + stream compaction [ES-dLLM §2.B top-k; DyLLM §2.A threshold].
- * Per sequence b, the selected set is force[b,:] plus
- *   TOPK:      the k best non-forced positions by (score descending, position ascending), where
+/* (2) Selection + stream compaction [ES-dLLM §2.B top-k; DyLLM §2.A threshold; DyLLM §2.C
+ * response-only steps leave the prompt out of the candidates].
+ * Flag byte force[b,s]: bit 0 set = forced (always selected); else bit 1 set = excluded (never
+ * selected); else a candidate. Other bits are ignored. NULL: every position is a candidate.
+ * Per sequence b, the selected set is the forced positions plus
+ *   TOPK:      the k best candidates by (score descending, position ascending), where
  *              NaN ranks below -inf and -0 equals +0 (fewer than k candidates -> all of them);
- *   THRESHOLD: the non-forced positions with score > tau (float32 compare; NaN never passes).
+ *   THRESHOLD: the candidates with score > tau (float32 compare; NaN never passes).
  * Output: sel_idx[row_ptr[b] .. row_ptr[b+1]) holds the flat ids b*S + s of sequence b in
  * ascending order; row_ptr[0] = 0, row_ptr[B] = total count M. Bit-exact and deterministic.
- * score : [B,S] float32; force : [B,S] uint8 (nonzero = forced) or NULL.
+ * score : [B,S] float32; force : [B,S] uint8 flags or NULL.
  * sel_idx : int32 [B*S] (entries past row_ptr[B] untouched); row_ptr : int32 [B+1].
  * S <= DLLM_MAX_SELECT_S, else DLLM_ERR_UNSUPPORTED. k >= 0; tau not NaN.
  * Workspace: none (ws may be NULL). */
@@ -205,6 +208,12 @@ dllm_status dllm_gather_kv_rows(const dllm_shape* shape, const void* k_cache, co
  * The result for every token is the attention of q_all (after the update) against the updated
  * cache, up to rounding, provided the state held that attention for the previous cache.
  * Initialise the state with a call that selects every position (then nothing is "other").
+ * q_first (0 <= q_first <= S) [DyLLM §2.C response-only steps]: unselected positions s < q_first
+ * of every sequence are not processed (their query and state are left as they are; o_all there
+ * is rewritten from the unchanged state, i.e. the same context as before), so a prompt held at
+ * the front of each sequence costs no attention work in such a step. Their state then no longer
+ * matches the cache; a later call that selects them (a step that re-injects the prompt)
+ * recomputes it exactly. 0 = every position.
  * q_sel : [m_cap, H hd]; q_all : [B, S, H hd] (updated in place); k_cache, v_cache :
  * [B, Hkv, S, hd]; k_old, v_old : [m_cap, Hkv, hd]; st_m, st_l : [B, S, H] float32; st_o :
  * [B, S, H hd] float32 (updated in place); o_sel : [m_cap, H hd]; o_all : [B, S, H hd].
@@ -213,9 +222,9 @@ dllm_status dllm_gather_kv_rows(const dllm_shape* shape, const void* k_cache, co
 dllm_status dllm_salient_attn(const dllm_shape* shape, float scale, const void* q_sel,
                               void* q_all, const void* k_cache, const void* v_cache,
                               const void* k_old, const void* v_old, const int32_t* sel_idx,
-                              const int32_t* row_ptr, int32_t m_cap, float* st_m, float* st_l,
-                              float* st_o, void* o_sel, void* o_all, void* ws, size_t ws_bytes,
-                              void* stream);
+                              const int32_t* row_ptr, int32_t m_cap, int32_t q_first,
+                              float* st_m, float* st_l, float* st_o, void* o_sel, void* o_all,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* Compact copies of whole rows [DyLLM §2.A: the FFN runs for the tokens whose context changed;
  * this gathers their contexts from the context of every token into the compact rows the FFN call

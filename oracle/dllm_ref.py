@@ -23,7 +23,9 @@ It computes, slowly and in float64, what the five library calls compute:
                       stable tokens the weights of unchanged keys are reused and only the changed
                       keys' contributions are replaced, which equals attention of the reused query
                       against the updated cache (see the function); gather_kv_rows copies the K/V
-                      rows that a step is about to overwrite.
+                      rows that a step is about to overwrite. DyLLM §2.C response-only steps:
+                      select_compact's excluded flag and salient_attention's q_first leave the
+                      prompt out of a step.
 
 Readings where the pages are silent (all listed in the design notes): confidence c is the maximum
 softmax probability of the previous-step logits at temperature 1; the transformer block is
@@ -131,19 +133,24 @@ def _rank_key(value: float, pos: int):
 
 
 def select_compact(score, force, mode: int, tau: float = 0.0, k: int = 0):
-    """Per sequence: forced positions plus top-k (or score > tau) of the rest, ascending.
+    """Per sequence: forced positions plus top-k (or score > tau) of the candidates, ascending.
 
     tau is taken as a float32, the type of the score array, so the comparison is float32.
 
-    score: float32 [B, S]; force: bool [B, S] or None.
+    score: float32 [B, S]; force: integer flags [B, S] or None: bit 0 forced, else bit 1
+    excluded (never selected: the prompt of a response-only step, DyLLM French summary page
+    §2.C), else a candidate. A bool array is forced / candidate.
     Returns (sel_idx int32 [M] with flat ids b*S + s, row_ptr int32 [B+1]).
     """
     score = np.asarray(score, dtype=np.float32)
     B, S = score.shape
+    flags = None if force is None else np.asarray(force).astype(np.int64)
     sel, row_ptr = [], [0]
     for b in range(B):
-        forced = [bool(force[b, s]) if force is not None else False for s in range(S)]
-        cand = [s for s in range(S) if not forced[s]]
+        forced = [bool(flags[b, s] & 1) if flags is not None else False for s in range(S)]
+        excluded = [bool(flags[b, s] & 2) and not forced[s] if flags is not None else False
+                    for s in range(S)]
+        cand = [s for s in range(S) if not forced[s] and not excluded[s]]
         if mode == SEL_TOPK:
             ranked = sorted(cand, key=lambda s: _rank_key(float(score[b, s]), s))
             chosen = ranked[: max(0, int(k))]
@@ -267,7 +274,7 @@ def context_all(q_all, k_cache, v_cache, H: int, Hkv: int, hd: int, scale: float
 
 
 def salient_attention(q_sel, q_all, k_cache, v_cache, sel_idx, row_ptr, H: int, Hkv: int,
-                      hd: int, scale: float):
+                      hd: int, scale: float, q_first: int = 0, o_prev=None, lse_prev=None):
     """DyLLM (French page) §2.B, both paths of one step, given the caches after the projection
     call of the step overwrote the K/V rows of the selected tokens:
       salient tokens (selected): their query is the one just projected and their attention row
@@ -278,6 +285,8 @@ def salient_attention(q_sel, q_all, k_cache, v_cache, sel_idx, row_ptr, H: int, 
         attention of the reused query against the updated cache.
     So the context of every token is the attention of the query cache, with the selected rows
     replaced, against the updated K/V cache.
+    Response-only steps (§2.C): unselected positions s < q_first are not processed; they keep
+    o_prev and lse_prev (their context and log-sum-exp before the step).
 
     Returns (q_all' [B, S, H*hd], o [B, S, H*hd], lse [B, S, H]).
     """
@@ -287,6 +296,13 @@ def salient_attention(q_sel, q_all, k_cache, v_cache, sel_idx, row_ptr, H: int, 
     ids = np.asarray(sel_idx[:M], dtype=np.int64)
     q_new[ids // S, ids % S] = np.asarray(q_sel, dtype=np.float64)[:M]
     o, lse = context_all(q_new, k_cache, v_cache, H, Hkv, hd, scale)
+    if q_first > 0:
+        skip = np.zeros((B, S), dtype=bool)
+        skip[:, :q_first] = True
+        skip[ids // S, ids % S] = False
+        if skip.any():   # (o_prev / lse_prev may be None when every position there is selected)
+            o[skip] = np.asarray(o_prev, dtype=np.float64)[skip]
+            lse[skip] = np.asarray(lse_prev, dtype=np.float64)[skip]
     return q_new, o, lse
 
 

@@ -181,9 +181,13 @@ def test_context_call_validation():
     assert rc(c, long, 0.1, *full, P, P, 128, P, P, P, P, P, ws) == tsp.DLLM_ERR_UNSUPPORTED
     lib = tsp.library()
     need = tsp.dllm_workspace_bytes(tsp.OP_ATTN, s, 128)
-    st = lib.dllm_salient_attn(ctypes.byref(s), 0.1, P, P, P, P, P, P, P, P, 128, P, P, P, P, P,
-                               P, need - 1, None)
+    st = lib.dllm_salient_attn(ctypes.byref(s), 0.1, P, P, P, P, P, P, P, P, 128, 0, P, P, P, P,
+                               P, P, need - 1, None)
     assert st == tsp.DLLM_ERR_WORKSPACE
+    for q_first in (-1, s.S + 1):   # outside [0, S]
+        st = lib.dllm_salient_attn(ctypes.byref(s), 0.1, P, P, P, P, P, P, P, P, 128, q_first, P,
+                                   P, P, P, P, P, need, None)
+        assert st == tsp.DLLM_ERR_INVALID_ARG
 
 
 def test_gather_rows_validation():

@@ -108,6 +108,26 @@ def test_select_topk_bit_exact(lib, kind, B, S, k):
 
 
 @pytest.mark.parametrize("kind", ["mixed", "ties", "random"])
+@pytest.mark.parametrize("B,S,k", [(1, 1024, 128), (3, 40, 5), (2, 1000, 37), (1, 8192, 64),
+                                   (4, 2048, 10 ** 6)])
+def test_select_excluded_positions_bit_exact(lib, kind, B, S, k):
+    """Flags: bit 0 forced, bit 1 excluded (a prompt half, random holes), forced wins, other bits
+    ignored; top-k and threshold."""
+    print(f"select flags kind={kind} B={B} S={S} k={k}", flush=True)
+    score = synth.adversarial_scores(B, S, seed=700 + S + k, kind=kind)
+    rng = np.random.default_rng(S + k + 1)
+    flags = np.zeros((B, S), dtype=np.uint8)
+    flags[:, : S // 2] = 2
+    flags[rng.random((B, S)) < 0.05] |= 1
+    flags[rng.random((B, S)) < 0.05] |= 2
+    flags[rng.random((B, S)) < 0.05] |= 4
+    if B > 1:
+        flags[-1, :] = 2
+    check_select(lib, score, flags, O.SEL_TOPK, k=k)
+    check_select(lib, score, flags, O.SEL_THRESHOLD, tau=0.0)
+
+
+@pytest.mark.parametrize("kind", ["mixed", "ties", "random"])
 @pytest.mark.parametrize("tau", [0.0, 0.5, -0.25, float("inf"), -float("inf")])
 def test_select_threshold_bit_exact(lib, kind, tau):
     B, S = 3, 1500

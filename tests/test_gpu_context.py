@@ -148,3 +148,70 @@ def test_no_selection_keeps_every_context(lib):
     torch.cuda.synchronize()
     assert_close(host(st_o), o0, 1e-6, "state o")
     assert_close(host(o_all), o0, TOL[BF16], "o_all")
+
+
+def test_response_only_steps_leave_the_prompt_alone(lib):
+    """DyLLM §2.C: with q_first = P the unselected prompt positions are not processed (query,
+    state and context bit-identical to before), response positions are updated, and a step that
+    selects every prompt position (the prompt re-injected) brings the prompt rows back to the
+    exact context of the updated cache. The oracle carries its own previous context for the
+    rows a step leaves out."""
+    B, S, H, Hkv, hd, P = 2, 160, 4, 2, 128, 96
+    Nq = H * hd
+    scale = 1.0 / math.sqrt(hd)
+    shape = lib.Shape(B=B, S=S, d=Nq, H=H, Hkv=Hkv, hd=hd, F=64, dtype="bf16")
+    q_all = synth.normal((B, S, Nq), 1.0, 770, BF16, "cuda")
+    kc = synth.normal((B, Hkv, S, hd), 1.0, 771, BF16, "cuda")
+    vc = synth.normal((B, Hkv, S, hd), 1.0, 772, BF16, "cuda")
+    st_m, st_l, st_o = exact_state(q_all, kc, vc, H, Hkv, hd, scale)
+    o_all = st_o.to(BF16).reshape(B, S, Nq).contiguous()
+    o_prev, lse_prev = O.context_all(host(q_all), host(kc), host(vc), H, Hkv, hd, scale)
+    rng = np.random.default_rng(773)
+    # per step: (response positions per sequence, prompt positions per sequence)
+    plan = [([20, 9], [0, 0]), ([5, 30], [1, 0]), ([12, 3], [P, P]), ([0, 7], [0, 0])]
+    for t, (n_resp, n_prompt) in enumerate(plan):
+        ids = []
+        for b in range(B):
+            pos = np.concatenate([rng.choice(P, n_prompt[b], replace=False),
+                                  P + rng.choice(S - P, n_resp[b], replace=False)])
+            ids.append(b * S + np.sort(pos))
+        sel = np.concatenate(ids).astype(np.int32)
+        rp = np.array([0] + list(np.cumsum([len(i) for i in ids])), np.int32)
+        M = int(rp[-1])
+        print(f"response-only step {t}: {M} selected ({sum(n_prompt)} prompt)", flush=True)
+        m_cap = max(M, 1)
+        sel_d = to_dev(sel if M else np.zeros(1, np.int32))
+        rp_d = to_dev(rp)
+        k_old = torch.empty(m_cap, Hkv, hd, dtype=BF16, device="cuda")
+        v_old = torch.empty_like(k_old)
+        lib.dllm_gather_kv_rows(shape, kc, vc, sel_d, rp_d, m_cap, k_old, v_old)
+        bs = torch.from_numpy(sel // S).long().cuda()
+        ss = torch.from_numpy(sel % S).long().cuda()
+        if M:
+            kc[bs, :, ss, :] = synth.normal((M, Hkv, hd), 1.0, 780 + t, BF16, "cuda")
+            vc[bs, :, ss, :] = synth.normal((M, Hkv, hd), 1.0, 790 + t, BF16, "cuda")
+        q_sel = synth.normal((m_cap, Nq), 1.0, 800 + t, BF16, "cuda")
+        q_before = q_all.clone()
+        before = [x.clone() for x in (st_m, st_l, st_o, o_all)]
+        o_sel = torch.empty(m_cap, Nq, dtype=BF16, device="cuda")
+        lib.dllm_salient_attn(shape, scale, q_sel, q_all, kc, vc, k_old, v_old, sel_d, rp_d,
+                              m_cap, st_m, st_l, st_o, o_sel, o_all,
+                              lib.workspace(lib.OP_ATTN, shape, m_cap), q_first=P)
+        torch.cuda.synchronize()
+        q_ref, o_ref, lse_ref = O.salient_attention(host(q_sel)[:M], host(q_before), host(kc),
+                                                    host(vc), sel, rp, H, Hkv, hd, scale,
+                                                    q_first=P, o_prev=o_prev, lse_prev=lse_prev)
+        skip = torch.zeros(B, S, dtype=torch.bool, device="cuda")
+        skip[:, :P] = True
+        if M:
+            skip[bs, ss] = False
+        for x, x0 in zip((st_m, st_l, st_o, o_all), before):
+            assert same_bits(x.reshape(B, S, -1)[skip], x0.reshape(B, S, -1)[skip])
+        assert same_bits(q_all[skip], q_before[skip])
+        assert_close(host(o_all), o_ref, TOL[BF16], f"step {t} o_all")
+        assert_close(host(st_o), o_ref, TOL[BF16], f"step {t} state o")
+        lse = (host(st_m) + np.log2(host(st_l))) * LN2
+        assert_close(lse, lse_ref, 1e-3, f"step {t} log-sum-exp")
+        o_prev, lse_prev = o_ref, lse_ref
+    # after the re-injection step every prompt row is exact again (and stays so in the last step,
+    # which changed keys but left the prompt out: the oracle keeps its step-3 rows as well)

@@ -90,9 +90,11 @@ def _check_topk(score, force, k, sel, row_ptr):
         assert np.all(np.diff(ids) > 0), "ascending, no duplicates"
         pos = set(int(i) - b * S for i in ids)
         assert all(0 <= p < S for p in pos)
-        forced = {s for s in range(S) if force is not None and force[b, s]}
-        cand = [s for s in range(S) if s not in forced]
-        assert forced <= pos
+        fl = [int(force[b, s]) if force is not None else 0 for s in range(S)]
+        forced = {s for s in range(S) if fl[s] & 1}
+        excluded = {s for s in range(S) if fl[s] & 2 and not fl[s] & 1}
+        cand = [s for s in range(S) if s not in forced and s not in excluded]
+        assert forced <= pos and not (excluded & pos)
         chosen = pos - forced
         assert len(chosen) == min(k, len(cand))
 
@@ -118,6 +120,31 @@ def test_topk_is_the_best_k_by_pairwise_order(kind, k):
     force[2, :] = True
     sel, row_ptr = O.select_compact(score, force, O.SEL_TOPK, k=k)
     _check_topk(score, force, k, sel, row_ptr)
+
+
+@pytest.mark.parametrize("kind", ["mixed", "equal", "ties", "random"])
+@pytest.mark.parametrize("k", [0, 1, 5, 17, 40])
+def test_topk_with_excluded_positions(kind, k):
+    """Flag bit 1 takes a position out of the candidates (a response-only step's prompt),
+    bit 0 (forced) wins over it, other bits are ignored."""
+    score = synth.adversarial_scores(4, 40, seed=31 + k, kind=kind).numpy()
+    flags = np.zeros((4, 40), dtype=np.uint8)
+    flags[0, :20] = 2                 # a 20-token prompt
+    flags[1, 10:30] = 2
+    flags[1, [3, 12]] = 3             # forced wins
+    flags[2, :] = 6                   # every position excluded (bit 2 ignored)
+    flags[3, ::3] = 4                 # ignored bit: still candidates
+    flags[3, 1] = 5                   # forced
+    sel, row_ptr = O.select_compact(score, flags, O.SEL_TOPK, k=k)
+    _check_topk(score, flags, k, sel, row_ptr)
+    assert row_ptr[3] == row_ptr[2]   # nothing from the fully excluded sequence
+
+
+def test_threshold_with_excluded_positions():
+    score = np.array([[0.9, 0.8, 0.1, 0.7, 0.95, 0.0]], dtype=np.float32)
+    flags = np.array([[2, 3, 2, 0, 0, 1]], dtype=np.uint8)
+    sel, rp = O.select_compact(score, flags, O.SEL_THRESHOLD, tau=0.5)
+    assert list(sel) == [1, 3, 4, 5] and list(rp) == [0, 4]
 
 
 def test_topk_signed_zero_and_nan_ties():
@@ -344,6 +371,36 @@ def test_salient_attention_rows_use_the_right_query():
     for r, flat in enumerate(rest):
         assert np.allclose(o[flat // S, flat % S], want_rest[r], rtol=1e-13)
         assert np.array_equal(q_new[flat // S, flat % S], q_all[flat // S, flat % S])
+
+
+def test_response_only_rows_before_q_first():
+    """q_first: unselected positions before it keep the given previous context and log-sum-exp,
+    selected ones there are exact, positions from q_first on are as without it."""
+    B, S, H, Hkv, hd, P = 2, 7, 2, 1, 3, 4
+    rng = np.random.default_rng(8)
+    q_all = rng.standard_normal((B, S, H * hd))
+    kc = rng.standard_normal((B, Hkv, S, hd))
+    vc = rng.standard_normal((B, Hkv, S, hd))
+    o_prev = rng.standard_normal((B, S, H * hd))
+    lse_prev = rng.standard_normal((B, S, H))
+    sel = np.array([1, 5, 7 + 6], np.int32)          # a prompt position of sequence 0
+    rp = np.array([0, 2, 3], np.int32)
+    q_sel = rng.standard_normal((3, H * hd))
+    q0, o0, l0 = O.salient_attention(q_sel, q_all, kc, vc, sel, rp, H, Hkv, hd, 0.3)
+    q1, o1, l1 = O.salient_attention(q_sel, q_all, kc, vc, sel, rp, H, Hkv, hd, 0.3, q_first=P,
+                                     o_prev=o_prev, lse_prev=lse_prev)
+    assert np.array_equal(q0, q1)
+    for b in range(B):
+        for s in range(S):
+            if s < P and b * S + s not in (1, 5, 13):
+                assert np.array_equal(o1[b, s], o_prev[b, s])
+                assert np.array_equal(l1[b, s], lse_prev[b, s])
+            else:
+                assert np.array_equal(o1[b, s], o0[b, s]) and np.array_equal(l1[b, s], l0[b, s])
+    # q_first = S and nothing selected: the previous contexts come back unchanged
+    _, o2, l2 = O.salient_attention(q_sel[:0], q_all, kc, vc, sel[:0], np.zeros(3, np.int32), H,
+                                    Hkv, hd, 0.3, q_first=S, o_prev=o_prev, lse_prev=lse_prev)
+    assert np.array_equal(o2, o_prev) and np.array_equal(l2, lse_prev)
 
 
 def test_stable_rows_equal_reused_weights_plus_changed_contributions():

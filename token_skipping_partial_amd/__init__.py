@@ -83,7 +83,8 @@ def _load():
         "dllm_partial_attn": (I32, [SP, F, P, P, P, P, P, I32, P, P, SZ, P]),
         "dllm_gather_ffn_scatter": (I32, [SP, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]),
         "dllm_gather_kv_rows": (I32, [SP, P, P, P, P, I32, P, P, P]),
-        "dllm_salient_attn": (I32, [SP, F, P, P, P, P, P, P, P, P, I32, P, P, P, P, P, P, SZ, P]),
+        "dllm_salient_attn": (I32, [SP, F, P, P, P, P, P, P, P, P, I32, I32, P, P, P, P, P, P, SZ,
+                                    P]),
         "dllm_gather_rows": (I32, [SP, P, I32, P, P, I32, P, P]),
         "dllm_workspace_bytes": (SZ, [I32, SP, I32]),
         "dllm_status_string": (ctypes.c_char_p, [I32]),
@@ -199,11 +200,14 @@ def dllm_gather_kv_rows(shape, k_cache, v_cache, sel_idx, row_ptr, m_cap, k_rows
 
 
 def dllm_salient_attn(shape, scale, q_sel, q_all, k_cache, v_cache, k_old, v_old, sel_idx,
-                      row_ptr, m_cap, st_m, st_l, st_o, o_sel, o_all, ws, stream=None):
+                      row_ptr, m_cap, st_m, st_l, st_o, o_sel, o_all, ws, stream=None, q_first=0):
+    """q_first (keyword here, after m_cap in the C call): unselected positions before it are
+    left out of the step (response-only steps)."""
     wp, wn = _ws(ws)
     _check(_lib.dllm_salient_attn(ctypes.byref(shape), float(scale), _ptr(q_sel), _ptr(q_all),
                                   _ptr(k_cache), _ptr(v_cache), _ptr(k_old), _ptr(v_old),
-                                  _ptr(sel_idx), _ptr(row_ptr), int(m_cap), _ptr(st_m),
+                                  _ptr(sel_idx), _ptr(row_ptr), int(m_cap), int(q_first),
+                                  _ptr(st_m),
                                   _ptr(st_l), _ptr(st_o), _ptr(o_sel), _ptr(o_all), wp, wn,
                                   _stream(stream)), "dllm_salient_attn")
 

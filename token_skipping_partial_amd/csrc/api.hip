@@ -51,7 +51,7 @@ dllm_status ws_status(const void* ws, size_t have, size_t need) {
 extern "C" {
 
 static_assert(DLLM_MAX_SALIENT_S == kSalientMaxS, "stable-token pass limit");
-int32_t dllm_version(void) { return 102; }
+int32_t dllm_version(void) { return 103; }
 
 const char* dllm_status_string(int32_t status) {
   switch (status) {
@@ -238,13 +238,14 @@ dllm_status dllm_gather_kv_rows(const dllm_shape* shape, const void* k_cache, co
 dllm_status dllm_salient_attn(const dllm_shape* shape, float scale, const void* q_sel,
                               void* q_all, const void* k_cache, const void* v_cache,
                               const void* k_old, const void* v_old, const int32_t* sel_idx,
-                              const int32_t* row_ptr, int32_t m_cap, float* st_m, float* st_l,
-                              float* st_o, void* o_sel, void* o_all, void* ws, size_t ws_bytes,
-                              void* stream) {
+                              const int32_t* row_ptr, int32_t m_cap, int32_t q_first, float* st_m,
+                              float* st_l, float* st_o, void* o_sel, void* o_all, void* ws,
+                              size_t ws_bytes, void* stream) {
   dllm_status st = layer_shape_status(shape, m_cap);
   if (st != DLLM_OK) return st;
   if (!q_sel || !q_all || !k_cache || !v_cache || !k_old || !v_old || !sel_idx || !row_ptr ||
-      !st_m || !st_l || !st_o || !o_sel || !o_all || !isfinite(scale))
+      !st_m || !st_l || !st_o || !o_sel || !o_all || !isfinite(scale) || q_first < 0 ||
+      q_first > shape->S)
     return DLLM_ERR_INVALID_ARG;
   for (const void* p : {q_sel, (const void*)q_all, k_cache, v_cache, k_old, v_old,
                         (const void*)st_o, (const void*)o_sel, (const void*)o_all})
@@ -253,8 +254,8 @@ dllm_status dllm_salient_attn(const dllm_shape* shape, float scale, const void* 
   const ProjShape p = proj_shape(shape, m_cap);
   if ((st = ws_status(ws, ws_bytes, attn_workspace_bytes(true, p))) != DLLM_OK) return st;
   return hip_status(launch_salient_attn(p, scale, q_sel, q_all, k_cache, v_cache, k_old, v_old,
-                                        sel_idx, row_ptr, st_m, st_l, st_o, o_sel, o_all, ws,
-                                        (hipStream_t)stream));
+                                        sel_idx, row_ptr, q_first, st_m, st_l, st_o, o_sel, o_all,
+                                        ws, (hipStream_t)stream));
 }
 
 dllm_status dllm_gather_rows(const dllm_shape* shape, const void* src, int32_t width,

@@ -52,6 +52,7 @@ struct AttnArgs {
   uint16_t* q_all;    // [B*S, H*hd]
   const uint16_t* k_old;  // [m_cap, Hkv, hd]
   const uint16_t* v_old;
+  int q_first;            // stable-token pass: positions q_first .. S-1 of every sequence
 };
 constexpr int kDeltaMaxS = kSalientMaxS;  // the changed-position list of a sequence lives in LDS
 
@@ -232,7 +233,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const int M = min(a.row_ptr[a.B], a.m_cap);
   const int r0 = min(a.row_ptr[b], M), r1 = min(a.row_ptr[b + 1], M);
   const int nA = r1 - r0;  // selected (changed) positions of the sequence
-  const int nrows = DELTA ? a.S * G : nA * G;
+  const int nrows = DELTA ? (a.S - a.q_first) * G : nA * G;
   const int tile0 = blockIdx.y * TQ;
   if (tile0 >= nrows) return;
   // key range [t0, t1) of this split; DELTA: entries [0, nA) of the changed list, 32 per tile
@@ -248,7 +249,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // token, or (DELTA) the flat position b*S + s
   const int qr = tile0 + 32 * wave + n;
   const bool qvalid = qr < nrows;
-  const int qj = qvalid ? (DELTA ? b * a.S + qr / G : r0 + qr / G) : 0;
+  const int qj = qvalid ? (DELTA ? b * a.S + a.q_first + qr / G : r0 + qr / G) : 0;
   const int qh = qvalid ? hk * G + qr % G : 0;
   const uint16_t* qsrc = DELTA ? a.q_all : a.q;
   bf16x8 qf[KK];
@@ -822,14 +823,32 @@ static hipError_t launch_exact_bf16(const ProjShape& s, float scale, const void*
 }
 
 // ---------------------------------------------------------------- context of every token
+// Positions before q_first (a prompt left out of a response-only step, DyLLM French summary page
+// §2.C): their state is not touched; the bf16 context is re-emitted from it, so o_all holds every
+// token's context after each call. One thread per 4 columns of a row.
+__global__ __launch_bounds__(256) void state_context_kernel(const float* st_o, uint16_t* o_all,
+                                                            int S, int q_first, int Nq,
+                                                            size_t total) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int c4 = Nq / 4;
+  const size_t row = idx / c4;             // b * q_first + s
+  const int c = (int)(idx - row * c4) * 4;
+  const size_t b = row / q_first, si = row - b * q_first;
+  const size_t off = (b * S + si) * Nq + c;
+  float v[4];
+  Elem<float>::load4(st_o + off, v);
+  Elem<uint16_t>::store4(o_all + off, v);
+}
+
 // DyLLM (French summary page) §2.B: stable tokens reuse their previous attention weights and take
 // in only the changed keys (pass 1, every position), salient tokens are recomputed exactly against
 // the updated cache (pass 2, the selected rows; it overwrites what pass 1 wrote at their positions).
 hipError_t launch_salient_attn(const ProjShape& s, float scale, const void* q_sel, void* q_all,
                                const void* k_cache, const void* v_cache, const void* k_old,
                                const void* v_old, const int32_t* sel_idx, const int32_t* row_ptr,
-                               float* st_m, float* st_l, float* st_o, void* o_sel, void* o_all,
-                               void* ws, hipStream_t st) {
+                               int q_first, float* st_m, float* st_l, float* st_o, void* o_sel,
+                               void* o_all, void* ws, hipStream_t st) {
   AttnArgs d{};
   d.kc = (const uint16_t*)k_cache; d.vc = (const uint16_t*)v_cache;
   d.row_ptr = row_ptr;
@@ -839,12 +858,20 @@ hipError_t launch_salient_attn(const ProjShape& s, float scale, const void* q_se
   d.sel_idx = sel_idx; d.st_m = st_m; d.st_l = st_l; d.st_o = st_o;
   d.o_all = (uint16_t*)o_all; d.q_all = (uint16_t*)q_all;
   d.k_old = (const uint16_t*)k_old; d.v_old = (const uint16_t*)v_old;
+  d.q_first = q_first;
+  if (q_first > 0) {
+    const size_t total = (size_t)s.B * q_first * (s.H * s.hd / 4);
+    hipLaunchKernelGGL(state_context_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       st, st_o, (uint16_t*)o_all, s.S, q_first, s.H * s.hd, total);
+  }
   const int G = s.H / s.Hkv;
-  const long rows = (long)s.S * G;
+  const long rows = (long)(s.S - q_first) * G;
   // eight waves (256 query rows) when that still gives a workgroup per CU, else four
   const int nw = (long)s.B * s.Hkv * cdiv(rows, 256) >= 256 ? 8 : 4;
   dim3 grid(s.B * s.Hkv, cdiv(rows, 32 * nw));
-  if (s.hd == 64) {
+  if (rows == 0) {
+    // every position before q_first: no stable-token pass
+  } else if (s.hd == 64) {
     if (nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8, 4, true>), grid, dim3(512), 0, st, d);
     else hipLaunchKernelGGL((attn_bf16_kernel<64, 4, 4, true>), grid, dim3(256), 0, st, d);
   } else {

@@ -88,8 +88,8 @@ hipError_t launch_attn(bool bf16, const ProjShape& s, float scale, const void* q
 hipError_t launch_salient_attn(const ProjShape& s, float scale, const void* q_sel, void* q_all,
                                const void* k_cache, const void* v_cache, const void* k_old,
                                const void* v_old, const int32_t* sel_idx, const int32_t* row_ptr,
-                               float* st_m, float* st_l, float* st_o, void* o_sel, void* o_all,
-                               void* ws, hipStream_t st);
+                               int q_first, float* st_m, float* st_l, float* st_o, void* o_sel,
+                               void* o_all, void* ws, hipStream_t st);
 hipError_t launch_gather_kv_rows(const ProjShape& s, size_t elem, const void* k_cache,
                                  const void* v_cache, const int32_t* sel_idx,
                                  const int32_t* row_ptr, void* k_rows, void* v_rows,

@@ -12,8 +12,11 @@
 // memory and no floating-point sum is involved: the result is bit-exact and deterministic.
 //
 // Each workgroup recomputes the selected counts of the sequences before it (a pass over their
-// force bytes, and over their scores in threshold mode) to find its output offset, so one
+// flag bytes, and over their scores in threshold mode) to find its output offset, so one
 // launch writes sel_idx and row_ptr with no inter-workgroup communication.
+//
+// Flag byte per position: bit 0 forced (always selected), bit 1 excluded (never a candidate, as
+// the prompt in DyLLM's response-only steps, French summary page §2.C); forced wins.
 #include "common.h"
 #include "kernels.h"
 
@@ -42,23 +45,29 @@ __device__ __forceinline__ int block_sum_int(int v, int* scratch) {
   return t;
 }
 
+// 0 candidate, 1 forced, 2 excluded
+__device__ __forceinline__ int pos_state(const SelectArgs& a, size_t i) {
+  const int fl = a.force ? a.force[i] : 0;
+  return (fl & 1) ? 1 : ((fl & 2) ? 2 : 0);
+}
+
 // number of positions sequence r contributes to the output
 __device__ int row_count(const SelectArgs& a, int r, int* scratch) {
-  int nf = 0, nt = 0;
+  int nf = 0, nt = 0;  // nf: forced + 65536 * excluded (S <= 8192)
   for (int s = threadIdx.x; s < a.S; s += kSelThreads) {
-    bool f = a.force && a.force[(size_t)r * a.S + s];
-    nf += f;
-    if (a.mode == 0 && !f) nt += a.score[(size_t)r * a.S + s] > a.tau;
+    const int st = pos_state(a, (size_t)r * a.S + s);
+    nf += st == 1 ? 1 : (st == 2 ? 65536 : 0);
+    if (a.mode == 0 && st == 0) nt += a.score[(size_t)r * a.S + s] > a.tau;
   }
   nf = block_sum_int(nf, scratch);
-  if (a.mode == 0) return nf + block_sum_int(nt, scratch);
-  return nf + min(a.k, a.S - nf);
+  if (a.mode == 0) return (nf & 65535) + block_sum_int(nt, scratch);
+  return (nf & 65535) + min(a.k, a.S - (nf & 65535) - (nf >> 16));
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   extern __shared__ uint32_t smem[];
   uint32_t* keys = smem;                                   // S
-  uint8_t* forced = reinterpret_cast<uint8_t*>(smem + a.S);  // S
+  uint8_t* state = reinterpret_cast<uint8_t*>(smem + a.S);  // S: 0 candidate, 1 forced, 2 excluded
   __shared__ int scratch[kSelWaves];
   __shared__ int wtot[2][kSelWaves];
   __shared__ uint32_t hist[256];
@@ -71,20 +80,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   int base = 0;
   for (int r = 0; r < b; ++r) base += row_count(a, r, scratch);
 
-  int nf = 0;
+  int nfx = 0;  // forced + 65536 * excluded
   for (int s = tid; s < S; s += kSelThreads) {
     float v = a.score[(size_t)b * S + s];
-    bool f = a.force && a.force[(size_t)b * S + s];
+    const int st = pos_state(a, (size_t)b * S + s);
     keys[s] = order_key(v);
-    forced[s] = f;
-    nf += f;
+    state[s] = (uint8_t)st;
+    nfx += st == 1 ? 1 : (st == 2 ? 65536 : 0);
   }
-  nf = block_sum_int(nf, scratch);  // contains __syncthreads: keys/forced visible after this
+  nfx = block_sum_int(nfx, scratch);  // contains __syncthreads: keys/state visible after this
 
   // ---- top-k: radix select of the kk-th largest candidate key T; `remaining` = how many keys
   // equal to T are taken (the lowest positions among them)
   const bool topk = a.mode == 1;
-  const int ncand = S - nf;
+  const int ncand = S - (nfx & 65535) - (nfx >> 16);
   const int kk = topk ? min(a.k, ncand) : 0;
   uint32_t T = 0xffffffffu;  // no key is above this one, and no key equals it
   uint32_t remaining = 0;
@@ -96,7 +105,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       __syncthreads();
       for (int s = tid; s < S; s += kSelThreads) {
         uint32_t key = keys[s];
-        if (!forced[s] && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        if (state[s] == 0 && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
       if (wave == 0) {
@@ -141,8 +150,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     const int s = c0 + tid;
     const bool in = s < S;
     const uint32_t key = in ? keys[s] : 0u;
-    const bool fr = in && forced[s];
-    const bool cand = in && !fr;
+    const int st = in ? state[s] : 2;
+    const bool fr = st == 1;
+    const bool cand = st == 0;
     const bool eq = topk && cand && key == T;
     const uint64_t eq_ball = __ballot(eq);
     if (lane == 0) wtot[0][wave] = __popcll(eq_ball);

@@ -181,14 +181,26 @@ class LayerAdaptiveModel:
       by the L1-normalised change of the layer-0 input against step t-1 (threshold `tau_in`).
     Buffers are sized for every token (the thresholded counts are only known on the device).
     The calls are told how many rows to plan for (`m_plan`): each row set's count of the last
-    step whose counts have reached the host, with a 1/8 margin. Counts come back by an
-    asynchronous copy, so no step waits for the device; a wrong guess costs speed, never rows.
+    step of the same kind whose counts have reached the host, with a 1/8 margin. Counts come back
+    by an asynchronous copy, so no step waits for the device; a wrong guess costs speed, never
+    rows.
+
+    Response-only steps (DyLLM §2.C), when `prompt_len` P > 0: positions 0..P-1 of every
+    sequence hold the prompt. A response-only step leaves them out of every row set (selection
+    flag "excluded") and out of the changed-key update of the contexts (`q_first` = P): their
+    caches, states, contexts and hidden rows keep what they held. Every `inject_every`-th step
+    (0 = never) re-injects the prompt: its positions are forced into every row set, so they are
+    recomputed exactly, layer by layer.
     """
 
     def __init__(self, shape: Shape, layers: list, tau_in: float, tau_ctx, scale=None,
-                 device="cuda"):
+                 device="cuda", prompt_len: int = 0, inject_every: int = 0):
         self.shape, self.layers = shape, layers
         self.tau_in = tau_in
+        if not 0 <= prompt_len <= shape.S:
+            raise ValueError(f"prompt_len {prompt_len} outside [0, S]")
+        self.prompt_len, self.inject_every = int(prompt_len), int(inject_every)
+        self.t = 0                                    # steps since fill
         self.scale = attn_scale(shape) if scale is None else scale
         L = len(layers)
         self.tau_ctx = list(tau_ctx) if isinstance(tau_ctx, (list, tuple)) else [tau_ctx] * L
@@ -211,7 +223,13 @@ class LayerAdaptiveModel:
         # workspaces sized for any m_plan (a nonzero m_plan in the shape asks for that size)
         self.scratch = LayerScratch(shape.with_plan(1), ntok, device)
         self.plan = [0] * (L + 1)                      # m_plan per row set (0: every token)
+        self._plans = {}                               # step kind (inject?) -> m_plan per set
         self._shapes = {}
+        self._counts_kind = False
+        flags = torch.zeros(B, S, dtype=torch.uint8, device=device)
+        flags[:, :prompt_len] = 2
+        self._flags_resp = flags if prompt_len else None     # prompt excluded
+        self._flags_inject = (flags // 2) if prompt_len else None  # prompt forced
         self._counts = torch.zeros(L + 1, dtype=torch.int32, device=device)
         self._counts_host = torch.zeros(L + 1, dtype=torch.int32,
                                         pin_memory=torch.device(device).type == "cuda")
@@ -232,7 +250,7 @@ class LayerAdaptiveModel:
             sh = self._shapes[m_plan] = self.shape.with_plan(m_plan)
         return sh
 
-    def _layer(self, l, sel_a, rp_a, sel_f, rp_f, tau, stream):
+    def _layer(self, l, sel_a, rp_a, sel_f, rp_f, tau, stream, flags=None):
         w, sc, n = self.layers[l], self.scratch, self.shape.B * self.shape.S
         sh = self._planned(self.plan[l])       # rows of set l: projection and attention
         sh_f = self._planned(self.plan[l + 1])  # rows of set l + 1: output projection and FFN
@@ -243,7 +261,8 @@ class LayerAdaptiveModel:
                                    sc.q_sel, self.k[l], self.v[l], sc.ws_qkv, stream)
         dllm_salient_attn(sh, self.scale, sc.q_sel, self.q_all[l], self.k[l], self.v[l],
                           self.k_old, self.v_old, sel_a, rp_a, n, self.st_m[l], self.st_l[l],
-                          self.st_o[l], sc.o_sel, cur, sc.ws_attn, stream)
+                          self.st_o[l], sc.o_sel, cur, sc.ws_attn, stream,
+                          q_first=self.prompt_len)
         if tau is None:   # every token (fill)
             sel_f.copy_(self.all_sel)
             rp_f.copy_(self.all_rp)
@@ -252,7 +271,7 @@ class LayerAdaptiveModel:
                           stream=stream)
             if self.layer_scores is not None:
                 self.layer_scores[l].copy_(self.score)
-            dllm_select_compact(sh, SEL_THRESHOLD, tau, 0, self.score, None, sel_f, rp_f,
+            dllm_select_compact(sh, SEL_THRESHOLD, tau, 0, self.score, flags, sel_f, rp_f,
                                 stream=stream)
         dllm_gather_rows(self.ctx_shape, cur, self.ctx_shape.d, sel_f, rp_f, n, self.o_rows,
                          stream)
@@ -263,7 +282,9 @@ class LayerAdaptiveModel:
     def fill(self, x0, stream=None):
         """Step 0: every layer on every token; primes caches, states and both context buffers."""
         self.plan = [0] * len(self.plan)
+        self._plans = {}
         self._counts_evt = None
+        self.t = 0
         self.hidden[0].copy_(x0)
         self.x_ref.copy_(x0)
         for l in range(len(self.layers)):
@@ -281,18 +302,24 @@ class LayerAdaptiveModel:
         elif not record:
             self.layer_scores = None
         self.cur = 1 - self.cur
+        self.t += 1
+        inject = self.inject_every > 0 and self.t % self.inject_every == 0
+        flags = None
+        if self.prompt_len:
+            flags = self._flags_inject if inject else self._flags_resp
         if self._counts_evt is not None and self._counts_evt.query():
-            self.plan = [c + c // 8 + 1 for c in self._counts_host.tolist()]
+            self._plans[self._counts_kind] = [c + c // 8 + 1 for c in self._counts_host.tolist()]
             self._counts_evt = None
+        self.plan = self._plans.get(inject, [0] * len(self.plan))
         self.hidden[0].copy_(x)
         dllm_saliency(self.shape, DELTA_L1N, 0.0, self.hidden[0], self.x_ref, None, self.score,
                       stream=stream)
-        dllm_select_compact(self.shape, SEL_THRESHOLD, self.tau_in, 0, self.score, None,
+        dllm_select_compact(self.shape, SEL_THRESHOLD, self.tau_in, 0, self.score, flags,
                             self.sel[0], self.rp[0], stream=stream)
         self.x_ref.copy_(x)
         for l in range(len(self.layers)):
             self._layer(l, self.sel[l], self.rp[l], self.sel[l + 1], self.rp[l + 1], taus[l],
-                        stream)
+                        stream, flags)
         if self._counts_evt is None:   # the previous copy has been read: send this step's counts
             B = self.shape.B
             with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
@@ -300,4 +327,5 @@ class LayerAdaptiveModel:
                 self._counts_host.copy_(self._counts, non_blocking=True)
                 self._counts_evt = torch.cuda.Event()
                 self._counts_evt.record()
+                self._counts_kind = inject
         return self.sel, self.rp
