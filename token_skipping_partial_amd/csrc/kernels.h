@@ -45,7 +45,10 @@ struct ProjShape {
 #define DLLM_WS_MAX_ROWS 256
 #endif
 constexpr int kWsMaxRows = DLLM_WS_MAX_ROWS;
-constexpr int kG32BigRows = 4096;
+#ifndef DLLM_G32_BIG_ROWS
+#define DLLM_G32_BIG_ROWS 4096
+#endif
+constexpr int kG32BigRows = DLLM_G32_BIG_ROWS;
 
 // launch plan of one GEMM: tile height, number of K splits
 struct GemmPlan {
