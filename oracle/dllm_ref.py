@@ -26,6 +26,9 @@ It computes, slowly and in float64, what the five library calls compute:
                       rows that a step is about to overwrite. DyLLM §2.C response-only steps:
                       select_compact's excluded flag and salient_attention's q_first leave the
                       prompt out of a step.
+  commit_step         SlowFast (German page) "Der SlowFast-Algorithmus" item 2: threshold commit
+                      of the active block with a top-k fallback; block advance; embed_rows writes
+                      the embeddings of the committed tokens (the next step's input rows).
 
 Readings where the pages are silent (all listed in the design notes): confidence c is the maximum
 softmax probability of the previous-step logits at temperature 1; the transformer block is
@@ -385,3 +388,77 @@ def selected_layer(h_in, wts: dict, sel_idx, row_ptr, k_cache, v_cache, h_out,
     out = gather_ffn_scatter(h_in, o_sel, wts["w_o"], wts["g_ffn"], wts["w_gate"], wts["w_up"],
                              wts["w_down"], sel_idx, row_ptr, h_out, eps)
     return q_sel, o_sel, k_new, v_new, out
+
+
+# ----------------------------------------------------------------------------------------------
+# device-side decode loop: commit rule, block advance, embeddings of committed tokens
+# ----------------------------------------------------------------------------------------------
+def confidence_argmax(logits_row):
+    """(largest softmax probability at temperature 1, index of the largest logit; the lowest
+    index among equal maxima) of one logit row: the token a masked position would take."""
+    z = np.asarray(logits_row, dtype=np.float64)
+    arg = int(np.argmax(z))          # numpy returns the first maximal index
+    return float(max_softmax_confidence(z[None])[0]), arg
+
+
+def commit_step(logits, tok, blk, prompt_len: int, block_len: int, tau: float, k_min: int):
+    """One commit of semi-autoregressive block decoding (SlowFast, German summary page,
+    "Der SlowFast-Algorithmus" item 2: tokens of the current region whose confidence is above a
+    high threshold are decoded together; when too few are, a top-k update keeps progress).
+
+    Per sequence b, with the active block [P + blk[b] L, P + (blk[b] + 1) L) (clipped to S):
+      m = its masked positions (tok < 0); for s in m, conf_s and arg_s from the logit row
+      (conf rounded to float32, the precision the decision is taken in);
+      commit C = the n best of m by (conf descending, position ascending), where
+      n = max(#{conf_s > tau}, min(k_min, |m|)); tok[b, s] = arg_s for s in C.
+    When the active block has no masked position left, blk[b] advances by one (at most to the
+    number of blocks, which means done). The next step's selection flags force the positions of
+    the (possibly new) active block.
+
+    logits [B, S, V]; tok int [B, S] (-1 = masked); blk int [B].
+    Returns (tok', blk', committed ids (flat b S + s, ascending per sequence), row_ptr,
+             flags uint8 [B, S]).
+    """
+    logits = np.asarray(logits)
+    tok = np.array(tok, dtype=np.int64, copy=True)
+    blk = np.array(blk, dtype=np.int64, copy=True)
+    B, S = tok.shape
+    nblk = -(-(S - prompt_len) // block_len)
+    tau32 = np.float32(tau)
+    sel, rp = [], [0]
+    flags = np.zeros((B, S), dtype=np.uint8)
+    for b in range(B):
+        if blk[b] < nblk:
+            lo = prompt_len + int(blk[b]) * block_len
+            hi = min(S, lo + block_len)
+            masked = [s for s in range(lo, hi) if tok[b, s] < 0]
+            conf, arg = {}, {}
+            for s in masked:
+                c, a = confidence_argmax(logits[b, s])
+                conf[s], arg[s] = np.float32(c), a
+            n_above = sum(1 for s in masked if conf[s] > tau32)
+            n = max(n_above, min(int(k_min), len(masked)))
+            order = sorted(masked, key=lambda s: (-float(conf[s]), s))
+            chosen = sorted(order[:n])
+            for s in chosen:
+                tok[b, s] = arg[s]
+            sel.extend(b * S + s for s in chosen)
+            if all(tok[b, s] >= 0 for s in range(lo, hi)):
+                blk[b] += 1
+        rp.append(len(sel))
+        if blk[b] < nblk:
+            lo = prompt_len + int(blk[b]) * block_len
+            flags[b, lo:min(S, lo + block_len)] = 1
+    return tok, blk, np.asarray(sel, np.int32), np.asarray(rp, np.int32), flags
+
+
+def embed_rows(emb, mask_emb, tok, sel_idx, row_ptr, x):
+    """x[b, s] = emb[tok[b, s]] for a committed token, the mask embedding for a masked one
+    (tok < 0), for the listed positions; other rows of x keep their values. Returns x'."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    S = x.shape[1]
+    for flat in np.asarray(sel_idx[:int(row_ptr[-1])], dtype=np.int64):
+        b, s = int(flat) // S, int(flat) % S
+        t = int(tok[b, s])
+        x[b, s] = np.asarray(emb[t] if t >= 0 else mask_emb, dtype=np.float64)
+    return x

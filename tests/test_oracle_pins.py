@@ -563,3 +563,103 @@ def test_kv_cache_sizing_matches_quoted_memory():
     within 5%, which supports the per-layer [B, Hkv, S, hd] bf16 layout at that shape."""
     bytes_kv = 2 * 32 * 1280 * 32 * 128 * 2
     assert abs(bytes_kv / 644e6 - 1.0) < 0.05
+
+
+# ---- decode loop: commit rule and block advance (SlowFast German page, "Der SlowFast-Algorithmus"
+# item 2: threshold commit with a top-k fallback), worked by hand on a 6-token vocabulary. One
+# logit a above five zeros gives the confidence e^a / (e^a + 5): a = 5 -> 0.967, 2 -> 0.596,
+# 1 -> 0.352 (tau = 0.9 needs a > ln 45 = 3.81).
+def _spike_logits(B, S, V, spikes):
+    z = np.zeros((B, S, V))
+    for (b, s), (a, idx) in spikes.items():
+        z[b, s, idx] = a
+    return z
+
+
+def test_confidence_argmax_closed_form_and_ties():
+    c, a = O.confidence_argmax(np.array([0.0, 0.0, 5.0, 0.0, 0.0, 0.0]))
+    assert a == 2 and abs(c - math.exp(5) / (math.exp(5) + 5)) < 1e-15
+    c, a = O.confidence_argmax(np.array([1.0, 3.0, 0.0, 3.0]))
+    assert a == 1 and abs(c - math.exp(3) / (2 * math.exp(3) + math.exp(1) + 1)) < 1e-15
+
+
+def test_commit_threshold_fallback_and_block_advance():
+    B, S, V, P, L = 2, 10, 6, 2, 4            # blocks [2, 6) and [6, 10)
+    tok = np.full((B, S), -1)
+    tok[:, :P] = [[1, 2], [4, 0]]
+    tok[1, 2:7] = [1, 1, 1, 1, 2]             # sequence 1: block 0 done, block 1 at position 6
+    blk = np.array([0, 1])
+    z = _spike_logits(B, S, V, {(0, 2): (5, 3), (0, 3): (2, 1), (0, 4): (5, 0), (0, 5): (1, 4),
+                                (1, 7): (1, 5), (1, 8): (2, 2), (1, 9): (1, 1)})
+    # two above the threshold in sequence 0 (k_min 1): both; none in sequence 1: the best one
+    t1, b1, sel, rp, fl = O.commit_step(z, tok, blk, P, L, 0.9, 1)
+    assert list(sel) == [2, 4, 10 + 8] and list(rp) == [0, 2, 3]
+    assert t1[0, 2] == 3 and t1[0, 4] == 0 and t1[1, 8] == 2 and t1[0, 3] == -1
+    assert list(b1) == [0, 1]
+    assert fl[0].tolist() == [0, 0, 1, 1, 1, 1, 0, 0, 0, 0] and fl[1].tolist() == [0] * 6 + [1] * 4
+    # k_min 2: sequence 0 completes block 0 (3 then 5 by confidence) and moves to block 1;
+    # sequence 1 takes 7 and 9 (equal confidence: both, as only two are left) and is done
+    t2, b2, sel, rp, fl = O.commit_step(z, t1, b1, P, L, 0.9, 2)
+    assert list(sel) == [3, 5, 10 + 7, 10 + 9] and list(rp) == [0, 2, 4]
+    assert t2[0, 3] == 1 and t2[0, 5] == 4 and t2[1, 7] == 5 and t2[1, 9] == 1
+    assert list(b2) == [1, 2]
+    assert fl[0].tolist() == [0] * 6 + [1] * 4 and not fl[1].any()
+    # a done sequence commits nothing and stays done
+    t3, b3, sel, rp, fl = O.commit_step(z, t2, b2, P, L, 0.9, 2)
+    assert list(rp) == [0, 0, 0] or rp[2] == rp[1]
+    assert b3[1] == 2 and np.array_equal(t3[1], t2[1])
+
+
+def test_commit_ties_go_to_the_lower_position_and_ragged_last_block():
+    B, S, V, P, L = 1, 9, 6, 2, 4             # blocks [2, 6), [6, 9)
+    tok = np.full((B, S), -1)
+    tok[0, :6] = [0, 0, 1, 1, 1, 1]
+    z = _spike_logits(B, S, V, {(0, 6): (1, 2), (0, 7): (1, 3), (0, 8): (1, 4)})
+    t, b, sel, rp, fl = O.commit_step(z, tok, np.array([1]), P, L, 0.9, 2)
+    assert list(sel) == [6, 7] and t[0, 6] == 2 and t[0, 7] == 3 and b[0] == 1
+    assert fl[0].tolist() == [0] * 6 + [1] * 3
+    t, b, sel, rp, fl = O.commit_step(z, t, b, P, L, 0.9, 2)
+    assert list(sel) == [8] and b[0] == 2 and not fl.any()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_commit_invariants_on_random_logits(seed):
+    rng = np.random.default_rng(seed)
+    B, S, V, P, L = 3, 40, 17, 8, 8
+    tok = np.full((B, S), -1)
+    tok[:, :P] = rng.integers(0, V, (B, P))
+    blk = np.array([0, 2, 3])
+    for b in range(B):
+        tok[b, P:P + blk[b] * L] = rng.integers(0, V, blk[b] * L)
+    z = rng.normal(0, 3, (B, S, V))
+    z[rng.random((B, S)) < 0.2, 0] += 30      # some rows far above the threshold
+    tok[1, P + 2 * L + 1] = 5                 # an already committed position inside a block
+    for k_min in (1, 3):
+        t, bl, sel, rp, fl = O.commit_step(z, tok, blk, P, L, 0.9, k_min)
+        for b in range(B):
+            lo, hi = P + blk[b] * L, min(S, P + (blk[b] + 1) * L)
+            masked = [s for s in range(lo, hi) if tok[b, s] < 0]
+            ids = [int(i) - b * S for i in sel[rp[b]:rp[b + 1]]]
+            conf = {s: np.float32(O.confidence_argmax(z[b, s])[0]) for s in masked}
+            above = [s for s in masked if conf[s] > np.float32(0.9)]
+            assert set(ids) <= set(masked)
+            assert len(ids) == max(len(above), min(k_min, len(masked)))
+            for s in ids:
+                assert t[b, s] == int(np.argmax(z[b, s]))
+                for u in set(masked) - set(ids):
+                    assert conf[s] > conf[u] or (conf[s] == conf[u] and s < u)
+            others = np.ones(S, bool)
+            others[ids] = False
+            assert np.array_equal(t[b][others], tok[b][others])
+            done = all(t[b, s] >= 0 for s in range(lo, hi))
+            assert bl[b] == blk[b] + (1 if done else 0)
+
+
+def test_embed_rows_copies_the_listed_rows():
+    rng = np.random.default_rng(3)
+    emb, mask = rng.standard_normal((7, 5)), rng.standard_normal(5)
+    tok = np.array([[3, -1, 6, 0]])
+    x = rng.standard_normal((1, 4, 5))
+    y = O.embed_rows(emb, mask, tok, np.array([1, 2], np.int32), np.array([0, 2], np.int32), x)
+    assert np.array_equal(y[0, 1], mask) and np.array_equal(y[0, 2], emb[6])
+    assert np.array_equal(y[0, 0], x[0, 0]) and np.array_equal(y[0, 3], x[0, 3])
