@@ -17,6 +17,12 @@
  *   dllm_salient_attn           exact rows for the selected tokens, changed-key update for the rest
  *   dllm_gather_rows            compact copies of selected rows (e.g. contexts for the FFN call)
  *
+ * and, for a decoding loop that stays on the device (block decoding, graph replay):
+ *
+ *   dllm_commit                 threshold / top-k commit of the active block, block advance,
+ *                               the next step's selection flags
+ *   dllm_embed_rows             embedding rows of listed (committed) positions
+ *
  * Sources (web pages; section names as printed there):
  *   [ES-dLLM]  "ES-dLLM: Efficient Inference for Diffusion Large Language Models by Early-Skipping",
  *              German summary page §2.A (importance-score equation, alpha = 0.5) and §2.B (top-k
@@ -27,7 +33,10 @@
  *              Partial Attention", French summary page §1 (bidirectional attention, each step a
  *              prefill-like pass), §2.A (cosine similarity of step t and t-1 vectors, salient below a
  *              threshold tau; FFN skipped for stable tokens), §2.B (attention rows of salient tokens
- *              recomputed exactly).
+ *              recomputed exactly), §2.C (response-only steps).
+ *   [SlowFast] "Accelerating Diffusion Large Language Models with SlowFast Sampling", German
+ *              summary page, "Der SlowFast-Algorithmus" item 2 (threshold commit with a top-k
+ *              fallback).
  *
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned, row-major and
@@ -73,7 +82,8 @@ typedef enum {
 typedef enum { DLLM_SEL_THRESHOLD = 0, DLLM_SEL_TOPK = 1 } dllm_sel_mode;
 
 typedef enum {
-  DLLM_OP_SALIENCY = 0, DLLM_OP_SELECT = 1, DLLM_OP_QKV = 2, DLLM_OP_ATTN = 3, DLLM_OP_FFN = 4
+  DLLM_OP_SALIENCY = 0, DLLM_OP_SELECT = 1, DLLM_OP_QKV = 2, DLLM_OP_ATTN = 3, DLLM_OP_FFN = 4,
+  DLLM_OP_COMMIT = 5
 } dllm_op;
 
 /* Model / batch shape. 48 bytes, no implicit padding.
@@ -236,8 +246,43 @@ dllm_status dllm_gather_rows(const dllm_shape* shape, const void* src, int32_t w
                              const int32_t* sel_idx, const int32_t* row_ptr, int32_t m_cap,
                              void* dst, void* stream);
 
+#define DLLM_MAX_BLOCK_LEN 256 /* largest block_len dllm_commit accepts */
+
+/* Commit step of semi-autoregressive block decoding [SlowFast §2 "Der SlowFast-Algorithmus"
+ * item 2: tokens of the current region above a high confidence threshold are decoded together,
+ * with a top-k update when too few are]. Sequence b decodes positions P .. S-1 (P = prompt_len)
+ * in blocks of block_len; blk[b] is its active block (blk[b] == number of blocks: done).
+ * For the masked positions s (tok[b,s] < 0) of the active block:
+ *   conf_s = largest softmax probability of logits[b,s,:] (temperature 1, float32),
+ *   arg_s  = index of the largest logit (the lowest one among equal maxima);
+ *   the n best by (conf descending, position ascending) commit, tok[b,s] = arg_s, with
+ *   n = max(#{conf_s > tau}, min(k_min, #masked)).
+ * A block left with no masked position advances blk[b] by one. Outputs: committed_idx
+ * [committed_rp[b] .. committed_rp[b+1]) the committed flat ids b*S + s of sequence b, ascending
+ * (capacity B * block_len); committed_rp [B+1]; flags [B,S] uint8 = 1 at the positions of the
+ * (new) active block, else 0 (the next step's forced selection, dllm_select_compact).
+ * logits : [B,S,V] dtype, V % 8 == 0 (else DLLM_ERR_UNSUPPORTED), 16-byte aligned; tok int32
+ * [B,S] and blk int32 [B] updated in place; 1 <= block_len <= DLLM_MAX_BLOCK_LEN; k_min >= 0;
+ * tau not NaN. The decision is taken on float32 confidences. Everything is read and written on
+ * the device: no host synchronisation. Workspace: dllm_workspace_bytes(DLLM_OP_COMMIT, shape,
+ * block_len). */
+dllm_status dllm_commit(const dllm_shape* shape, const void* logits, int32_t prompt_len,
+                        int32_t block_len, float tau, int32_t k_min, int32_t* tok, int32_t* blk,
+                        int32_t* committed_idx, int32_t* committed_rp, uint8_t* flags, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Embedding rows of listed positions [the next step's input after a commit]. For
+ * j < M = min(row_ptr[B], m_cap), with p = sel_idx[j] (flat b*S + s) and t = tok[p]:
+ *   x[p, :] = emb[t, :] if 0 <= t < V, else mask_emb (a masked position).
+ * emb : [V, d] dtype (V = shape->V); mask_emb : [d]; tok : int32 [B*S]; x : [B,S,d] dtype.
+ * d * element size must be a multiple of 16 bytes. Bit-exact copies. Workspace: none. */
+dllm_status dllm_embed_rows(const dllm_shape* shape, const void* emb, const void* mask_emb,
+                            const int32_t* tok, const int32_t* sel_idx, const int32_t* row_ptr,
+                            int32_t m_cap, void* x, void* stream);
+
 /* Bytes of device workspace the call `op` (a dllm_op) needs for this shape and m_cap; 0 when
- * none. With shape->m_plan == 0 the size is that of the plan for m_cap rows; with m_plan > 0 it
+ * none (for DLLM_OP_COMMIT the third argument is the block length).
+ * With shape->m_plan == 0 the size is that of the plan for m_cap rows; with m_plan > 0 it
  * covers every m_plan in [1, m_cap], so a caller may change m_plan from call to call without
  * reallocating. Returns (size_t)-1 for an invalid op or shape. Pure host function. */
 size_t dllm_workspace_bytes(int32_t op, const dllm_shape* shape, int32_t m_cap);

@@ -197,3 +197,32 @@ def test_gather_rows_validation():
     assert rc(g, s, P, 0, P, P, 128, P) == tsp.DLLM_ERR_INVALID_ARG
     assert rc(g, s, P, 4096, P, P, 1025, P) == tsp.DLLM_ERR_INVALID_ARG
     assert rc(g, s, P, 4, P, P, 128, P) == tsp.DLLM_ERR_UNSUPPORTED   # 8-byte rows
+
+
+def test_commit_and_embed_validation():
+    s = llada()
+    c, e = tsp.dllm_commit, tsp.dllm_embed_rows
+    need = tsp.dllm_workspace_bytes(tsp.OP_COMMIT, s, 32)
+    assert need >= 2 * 32 * 4
+    with pytest.raises(tsp.DllmError):
+        tsp.dllm_workspace_bytes(tsp.OP_COMMIT, s, tsp.MAX_BLOCK_LEN + 1)
+    args = lambda **k: [k.get("shape", s), k.get("logits", P), k.get("prompt", 512),  # noqa: E731
+                        k.get("block", 32), k.get("tau", 0.9), k.get("k", 1), P, P, P, P, P, P]
+    lib = tsp.library()
+    call = lambda a, wsb=need: lib.dllm_commit(ctypes.byref(a[0]), *a[1:], wsb, None)  # noqa
+    assert call(args(logits=None)) == tsp.DLLM_ERR_INVALID_ARG
+    assert call(args(prompt=-1)) == tsp.DLLM_ERR_INVALID_ARG
+    assert call(args(prompt=1025)) == tsp.DLLM_ERR_INVALID_ARG
+    assert call(args(block=0)) == tsp.DLLM_ERR_INVALID_ARG
+    assert call(args(k=-1)) == tsp.DLLM_ERR_INVALID_ARG
+    assert call(args(tau=float("nan"))) == tsp.DLLM_ERR_INVALID_ARG
+    assert call(args(logits=P + 4)) == tsp.DLLM_ERR_INVALID_ARG          # misaligned
+    assert call(args(block=tsp.MAX_BLOCK_LEN + 1)) == tsp.DLLM_ERR_UNSUPPORTED
+    odd = llada(); odd.V = 126460
+    assert call(args(shape=odd)) == tsp.DLLM_ERR_UNSUPPORTED            # V % 8 != 0
+    assert call(args(), need - 1) == tsp.DLLM_ERR_WORKSPACE
+    assert rc(e, s, None, P, P, P, P, 128, P) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(e, s, P, P, P, P, P, 1025, P) == tsp.DLLM_ERR_INVALID_ARG
+    assert rc(e, s, P + 8, P, P, P, P, 128, P) == tsp.DLLM_ERR_INVALID_ARG  # misaligned
+    small = tsp.Shape(B=1, S=16, d=4, H=1, Hkv=1, hd=64, F=64, dtype="bf16", V=10)
+    assert rc(e, small, P, P, P, P, P, 4, P) == tsp.DLLM_ERR_UNSUPPORTED  # 8-byte rows

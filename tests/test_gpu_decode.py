@@ -1,0 +1,256 @@
+"""Parity of the device-side decode-loop calls against the oracle (SlowFast German summary page,
+"Der SlowFast-Algorithmus" item 2: threshold commit with a top-k fallback; block decoding).
+
+dllm_commit is run step after step until every block is decoded; after each call the token
+ids, block indices, committed lists and flags must equal the oracle's bit for bit. The commit
+decision is taken on float32 confidences on both sides (the oracle rounds its float64 value), so
+the inputs keep every confidence more than 1e-4 (relative) from the threshold and from the
+confidence at the cut of the ranking, unless the two rows are identical (then the confidences
+are equal on both sides and the lower position wins). Logits: N(0, 3^2) (the long-context
+workload's recipe) with some rows given one logit raised by 30 (confidence ~1, above 0.9).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from parity import assert_close, host, same_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+TAU = 0.9
+
+
+class Rows:
+    """logits[b, s] -> host float64 row, read on demand (the full-vocabulary arrays are 1 GB)."""
+
+    def __init__(self, t):
+        self.t, self.cache = t, {}
+
+    def __getitem__(self, bs):
+        if bs not in self.cache:
+            self.cache[bs] = host(self.t[bs[0], bs[1]])
+        return self.cache[bs]
+
+
+def make_logits(B, S, V, seed, dtype, spike_frac=0.25, dup=None):
+    z = synth.normal((B, S, V), 3.0, seed, torch.float32, "cuda")
+    rng = np.random.default_rng(seed)
+    rows = np.argwhere(rng.random((B, S)) < spike_frac)
+    if len(rows):
+        idx = torch.from_numpy(rng.integers(0, V, len(rows))).cuda()
+        b = torch.from_numpy(rows[:, 0]).cuda()
+        s = torch.from_numpy(rows[:, 1]).cuda()
+        z[b, s, idx] += 30.0
+    if dup is not None:                       # identical rows: equal confidences
+        (b0, s0), (b1, s1) = dup
+        z[b1, s1] = z[b0, s0]
+    return z.to(dtype)
+
+
+def margins_ok(rows, tok, blk, P, L, S, k_min, nblk):
+    """The float32 decision is clear of rounding for every sequence (see the module notes)."""
+    for b in range(tok.shape[0]):
+        if blk[b] >= nblk:
+            continue
+        lo = P + blk[b] * L
+        masked = [s for s in range(lo, min(S, lo + L)) if tok[b, s] < 0]
+        conf = {s: O.confidence_argmax(rows[b, s])[0] for s in masked}
+        if any(abs(c - TAU) < 1e-4 * TAU for c in conf.values()):
+            return False
+        order = sorted(masked, key=lambda s: (-conf[s], s))
+        n = max(sum(c > TAU for c in conf.values()), min(k_min, len(masked)))
+        if 0 < n < len(order):
+            a, c = order[n - 1], order[n]
+            same = np.array_equal(rows[b, a], rows[b, c])
+            if not same and conf[a] - conf[c] < 1e-4 * conf[a]:
+                return False
+    return True
+
+
+CASES = {
+    # name: B, S, V, prompt, block, k_min, dtype, start blocks, identical rows
+    "tiny_bf16": (3, 40, 64, 8, 8, 2, torch.bfloat16, [0, 2, 3], ((0, 9), (0, 12))),
+    "tiny_f32": (3, 40, 64, 8, 8, 1, torch.float32, [0, 1, 3], None),
+    "ragged_tail": (2, 45, 128, 10, 8, 3, torch.bfloat16, [0, 3], ((1, 35), (1, 37))),
+    "block_256": (1, 600, 256, 88, 256, 16, torch.bfloat16, [0], None),
+    "long_context_full_vocab": (1, 4096, 126464, 3584, 32, 1, torch.bfloat16, [0], None),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_commit_steps_match_the_oracle(lib, case):
+    B, S, V, P, L, k_min, dtype, blk0, dup = CASES[case]
+    print(f"commit {case}", flush=True)
+    nblk = -(-(S - P) // L)
+    shape = lib.Shape(B=B, S=S, d=64, H=1, Hkv=1, hd=64, F=64,
+                      dtype="bf16" if dtype == torch.bfloat16 else "f32", V=V)
+    rng = np.random.default_rng(11)
+    tok = np.full((B, S), -1, np.int32)
+    for b in range(B):
+        tok[b, :P + blk0[b] * L] = rng.integers(0, V, P + blk0[b] * L)
+    tok[0, P + blk0[0] * L + 1] = 3          # a committed position inside an active block
+    blk = np.asarray(blk0, np.int32)
+    tok_d, blk_d = to_dev(tok), to_dev(blk)
+    cidx = torch.full((B * L,), -7, dtype=torch.int32, device="cuda")
+    crp = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    flags = torch.full((B, S), 9, dtype=torch.uint8, device="cuda")
+    ws = lib.workspace(lib.OP_COMMIT, shape, L)
+    max_steps = 3 if V > 10000 else 200
+    for step in range(max_steps):
+        if np.all(blk >= nblk):
+            break
+        for seed in range(1000 + 37 * step, 1000 + 37 * step + 30):
+            logits = make_logits(B, S, V, seed, dtype, dup=dup if step == 0 else None)
+            rows = Rows(logits)
+            if margins_ok(rows, tok, blk, P, L, S, k_min, nblk):
+                break
+        else:
+            pytest.fail("no seed with clear confidence margins")
+        lib.dllm_commit(shape, logits, P, L, TAU, k_min, tok_d, blk_d, cidx, crp, flags, ws)
+        torch.cuda.synchronize()
+        tok, blk, r_sel, r_rp, r_flags = O.commit_step(rows, tok, blk, P, L, TAU, k_min)
+        tok, blk = tok.astype(np.int32), blk.astype(np.int32)
+        assert np.array_equal(crp.cpu().numpy(), r_rp), (step, crp.cpu().numpy(), r_rp)
+        got = cidx.cpu().numpy()
+        assert np.array_equal(got[:r_rp[-1]], r_sel), step
+        assert np.array_equal(tok_d.cpu().numpy(), tok), step
+        assert np.array_equal(blk_d.cpu().numpy(), blk), step
+        assert np.array_equal(flags.cpu().numpy(), r_flags), step
+        del logits, rows
+    if V < 10000:
+        assert np.all(blk == nblk) and np.all(tok >= 0), "every block decoded"
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 64), (torch.float32, 32)])
+def test_embed_rows_copy_the_listed_rows(lib, dtype, d):
+    B, S, V = 2, 30, 50
+    print(f"embed rows {dtype} d={d}", flush=True)
+    shape = lib.Shape(B=B, S=S, d=d, H=1, Hkv=1, hd=64, F=64,
+                      dtype="bf16" if dtype == torch.bfloat16 else "f32", V=V)
+    emb = synth.normal((V, d), 1.0, 60, dtype, "cuda")
+    mask = synth.normal((d,), 1.0, 61, dtype, "cuda")
+    rng = np.random.default_rng(62)
+    tok = rng.integers(-1, V, (B, S)).astype(np.int32)
+    tok[0, 3], tok[1, 4], tok[1, 5] = V, V + 100, -5      # outside [0, V): the mask row
+    x = synth.normal((B, S, d), 1.0, 63, dtype, "cuda")
+    x0 = x.clone()
+    sel = np.sort(rng.choice(B * S, 23, replace=False)).astype(np.int32)
+    sel = np.unique(np.concatenate([sel, [3, 34, 35]])).astype(np.int32)
+    rp = np.array([0, int(np.sum(sel < S)), len(sel)], np.int32)
+    lib.dllm_embed_rows(shape, emb, mask, to_dev(tok), to_dev(sel), to_dev(rp), len(sel) + 4, x)
+    torch.cuda.synchronize()
+    tok_ref = np.where((tok >= 0) & (tok < V), tok, -1)
+    ref = O.embed_rows(host(emb), host(mask), tok_ref, sel, rp, host(x0))
+    assert np.array_equal(host(x), ref)
+    keep = np.ones(B * S, bool)
+    keep[sel] = False
+    assert same_bits(x.reshape(B * S, d)[torch.from_numpy(keep).cuda()],
+                     x0.reshape(B * S, d)[torch.from_numpy(keep).cuda()])
+
+
+# ---- the whole decoding loop (BlockDecoder): early-skip step with the active block forced, commit,
+# embeddings of the committed tokens. Saliency at the input (skip 0): unchanged positions have an
+# exact zero change on both sides and tie by position, changed ones are far above.
+DB, DS, Dd, DH, DHkv, Dhd, DF, DL, DV = 2, 48, 256, 4, 2, 64, 512, 3, 64
+DP, DBLK, DK, DKMIN = 16, 8, 4, 1
+EPS = 1e-5
+
+
+def decode_setup(lib, seed):
+    from token_skipping_partial_amd.step import (BlockDecoder, EarlySkipModel, LayerWeights,
+                                                 SelectConfig)
+    shape = lib.Shape(B=DB, S=DS, d=Dd, H=DH, Hkv=DHkv, hd=Dhd, F=DF, dtype="bf16", V=DV)
+    w = [synth.layer_weights(Dd, DH, DHkv, Dhd, DF, seed=seed + l, dtype=torch.bfloat16)
+         for l in range(DL)]
+    emb = synth.normal((DV, Dd), 1.0, seed + 50, torch.bfloat16, "cuda")
+    mask = synth.normal((Dd,), 1.0, seed + 51, torch.bfloat16, "cuda")
+    prompt = torch.from_numpy(np.random.default_rng(seed).integers(0, DV, (DB, DP))).int().cuda()
+    model = EarlySkipModel(shape, [LayerWeights.from_dict(x) for x in w], 0,
+                           SelectConfig(mode=lib.SEL_TOPK, k=DK, alpha=0.0), DB * (DK + DBLK))
+    dec = BlockDecoder(model, emb, mask, DP, DBLK, TAU, DKMIN)
+    dec.start(prompt)
+    return dec, w, emb, mask, prompt
+
+
+class OracleDecoder:
+    def __init__(self, w, emb, mask, prompt):
+        self.w = [{k: host(v) for k, v in wl.items()} for wl in w]
+        self.emb, self.mask = host(emb), host(mask)
+        self.tok = np.full((DB, DS), -1, np.int64)
+        self.tok[:, :DP] = prompt.cpu().numpy()
+        self.blk = np.zeros(DB, np.int64)
+        self.flags = np.zeros((DB, DS), np.uint8)
+        self.flags[:, DP:DP + DBLK] = 1
+        all_sel = np.arange(DB * DS, dtype=np.int32)
+        self.all_rp = np.arange(0, DB * DS + 1, DS, dtype=np.int32)
+        self.x = O.embed_rows(self.emb, self.mask, self.tok, all_sel, self.all_rp,
+                              np.zeros((DB, DS, Dd)))
+        self.k = [np.zeros((DB, DHkv, DS, Dhd)) for _ in range(DL)]
+        self.v = [np.zeros((DB, DHkv, DS, Dhd)) for _ in range(DL)]
+        self.h = [None] + [np.zeros((DB, DS, Dd)) for _ in range(DL)]
+        self.layers(all_sel, self.all_rp)
+        self.h_ref = self.x
+
+    def layers(self, sel, rp):
+        self.h[0] = self.x
+        for l in range(DL):
+            _, _, self.k[l], self.v[l], self.h[l + 1] = O.selected_layer(
+                self.h[l], self.w[l], sel, rp, self.k[l], self.v[l], self.h[l + 1], DH, DHkv,
+                Dhd, EPS, 1.0 / np.sqrt(Dhd))
+
+    def step(self, rows):
+        score, _, _ = O.saliency(self.x, self.h_ref, None, 0.0, O.DELTA_L1N)
+        sel, rp = O.select_compact(score, self.flags, O.SEL_TOPK, k=DK)
+        self.h_ref = self.x
+        self.layers(sel, rp)
+        self.tok, self.blk, c_sel, c_rp, self.flags = O.commit_step(rows, self.tok, self.blk, DP,
+                                                                    DBLK, TAU, DKMIN)
+        self.x = O.embed_rows(self.emb, self.mask, self.tok, c_sel, c_rp, self.x)
+        return sel, rp
+
+
+def test_decode_loop_matches_the_oracle(lib):
+    print("decode loop: 2 x 48 tokens (16 prompt, blocks of 8), 3 layers, 8 steps", flush=True)
+    dec, w, emb, mask, prompt = decode_setup(lib, 900)
+    ref = OracleDecoder(w, emb, mask, prompt)
+    nblk = -(-(DS - DP) // DBLK)
+    for t in range(8):
+        for seed in range(2000 + 31 * t, 2000 + 31 * t + 30):
+            logits = make_logits(DB, DS, DV, seed, torch.bfloat16, spike_frac=0.15)
+            rows = Rows(logits)
+            if margins_ok(rows, ref.tok, ref.blk, DP, DBLK, DS, DKMIN, nblk):
+                break
+        dec.step(logits)
+        torch.cuda.synchronize()
+        sel, rp = ref.step(rows)
+        s = dec.model.step1
+        assert np.array_equal(s.row_ptr.cpu().numpy(), rp), t
+        assert np.array_equal(s.sel_idx.cpu().numpy()[:rp[-1]], sel), t
+        assert np.array_equal(dec.tok.cpu().numpy(), ref.tok), t
+        assert np.array_equal(dec.blk.cpu().numpy(), ref.blk), t
+        assert np.array_equal(dec.flags.cpu().numpy(), ref.flags), t
+        assert np.array_equal(host(dec.x), ref.x), t
+        assert_close(host(dec.model.hidden[DL]), ref.h[DL], 2e-2, f"step {t} output")
+
+
+def test_decode_step_replays_from_a_graph(lib):
+    """A decoder replaying captured steps (one graph per logits buffer) against an identical one
+    run eagerly: every state tensor bit-identical after every step, with eager work and host
+    synchronisations between the replays."""
+    print("decode loop: graph replay vs eager, 10 steps", flush=True)
+    eager = decode_setup(lib, 910)[0]
+    graph = decode_setup(lib, 910)[0]
+    bufs = [make_logits(DB, DS, DV, 3000 + i, torch.bfloat16, spike_frac=0.15) for i in range(3)]
+    torch.cuda.synchronize()
+    graphs = [graph.capture(b) for b in bufs]
+    torch.cuda.synchronize()
+    for t in range(10):
+        eager.step(bufs[t % 3])
+        graphs[t % 3].replay()
+        torch.cuda.synchronize()
+        for a, b in ((eager.tok, graph.tok), (eager.blk, graph.blk), (eager.flags, graph.flags),
+                     (eager.x, graph.x), (eager.model.hidden[DL], graph.model.hidden[DL]),
+                     (eager.model.k[DL - 1], graph.model.k[DL - 1])):
+            assert torch.equal(a, b), t
+    assert int(eager.tok.ge(0).sum()) > DB * DP   # tokens were committed

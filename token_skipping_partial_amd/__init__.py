@@ -22,14 +22,15 @@ DLLM_OK, DLLM_ERR_INVALID_ARG, DLLM_ERR_UNSUPPORTED, DLLM_ERR_WORKSPACE, DLLM_ER
 F32, BF16 = 0, 1
 DELTA_L1N, DELTA_COS, DELTA_L2R = 0, 1, 2
 SEL_THRESHOLD, SEL_TOPK = 0, 1
-OP_SALIENCY, OP_SELECT, OP_QKV, OP_ATTN, OP_FFN = range(5)
+OP_SALIENCY, OP_SELECT, OP_QKV, OP_ATTN, OP_FFN, OP_COMMIT = range(6)
 MAX_SELECT_S = 8192
 MAX_SALIENT_S = 8192
+MAX_BLOCK_LEN = 256
 
 EXPORTS = ("dllm_saliency", "dllm_select_compact", "dllm_gather_qkv_scatter_kv",
            "dllm_partial_attn", "dllm_gather_ffn_scatter", "dllm_gather_kv_rows",
-           "dllm_salient_attn", "dllm_gather_rows", "dllm_workspace_bytes", "dllm_status_string",
-           "dllm_version")
+           "dllm_salient_attn", "dllm_gather_rows", "dllm_commit", "dllm_embed_rows",
+           "dllm_workspace_bytes", "dllm_status_string", "dllm_version")
 
 
 class DllmError(RuntimeError):
@@ -86,6 +87,8 @@ def _load():
         "dllm_salient_attn": (I32, [SP, F, P, P, P, P, P, P, P, P, I32, I32, P, P, P, P, P, P, SZ,
                                     P]),
         "dllm_gather_rows": (I32, [SP, P, I32, P, P, I32, P, P]),
+        "dllm_commit": (I32, [SP, P, I32, I32, F, I32, P, P, P, P, P, P, SZ, P]),
+        "dllm_embed_rows": (I32, [SP, P, P, P, P, P, I32, P, P]),
         "dllm_workspace_bytes": (SZ, [I32, SP, I32]),
         "dllm_status_string": (ctypes.c_char_p, [I32]),
         "dllm_version": (I32, []),
@@ -216,3 +219,18 @@ def dllm_gather_rows(shape, src, width, sel_idx, row_ptr, m_cap, dst, stream=Non
     _check(_lib.dllm_gather_rows(ctypes.byref(shape), _ptr(src), int(width), _ptr(sel_idx),
                                  _ptr(row_ptr), int(m_cap), _ptr(dst), _stream(stream)),
            "dllm_gather_rows")
+
+
+def dllm_commit(shape, logits, prompt_len, block_len, tau, k_min, tok, blk, committed_idx,
+                committed_rp, flags, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(_lib.dllm_commit(ctypes.byref(shape), _ptr(logits), int(prompt_len), int(block_len),
+                            float(tau), int(k_min), _ptr(tok), _ptr(blk), _ptr(committed_idx),
+                            _ptr(committed_rp), _ptr(flags), wp, wn, _stream(stream)),
+           "dllm_commit")
+
+
+def dllm_embed_rows(shape, emb, mask_emb, tok, sel_idx, row_ptr, m_cap, x, stream=None):
+    _check(_lib.dllm_embed_rows(ctypes.byref(shape), _ptr(emb), _ptr(mask_emb), _ptr(tok),
+                                _ptr(sel_idx), _ptr(row_ptr), int(m_cap), _ptr(x),
+                                _stream(stream)), "dllm_embed_rows")

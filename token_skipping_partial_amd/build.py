@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdllm.so")
-SOURCES = ["api.hip", "saliency.hip", "select.hip", "gemm.hip", "attn.hip"]
+SOURCES = ["api.hip", "saliency.hip", "select.hip", "gemm.hip", "attn.hip", "decode.hip"]
 ARCH = "gfx950"
 
 

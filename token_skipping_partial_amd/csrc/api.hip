@@ -51,7 +51,7 @@ dllm_status ws_status(const void* ws, size_t have, size_t need) {
 extern "C" {
 
 static_assert(DLLM_MAX_SALIENT_S == kSalientMaxS, "stable-token pass limit");
-int32_t dllm_version(void) { return 103; }
+int32_t dllm_version(void) { return 104; }
 
 const char* dllm_status_string(int32_t status) {
   switch (status) {
@@ -66,6 +66,9 @@ const char* dllm_status_string(int32_t status) {
 
 size_t dllm_workspace_bytes(int32_t op, const dllm_shape* shape, int32_t m_cap) {
   switch (op) {
+    case DLLM_OP_COMMIT:  // m_cap is the block length here
+      if (!base_shape_ok(shape) || m_cap < 1 || m_cap > kMaxBlockLen) return (size_t)-1;
+      return 2 * ((((size_t)shape->B * m_cap * 4) + 255) & ~(size_t)255);
     case DLLM_OP_SALIENCY:
       return base_shape_ok(shape) ? 0 : (size_t)-1;
     case DLLM_OP_SELECT:
@@ -271,4 +274,43 @@ dllm_status dllm_gather_rows(const dllm_shape* shape, const void* src, int32_t w
                                        (hipStream_t)stream));
 }
 
+
+dllm_status dllm_commit(const dllm_shape* shape, const void* logits, int32_t prompt_len,
+                        int32_t block_len, float tau, int32_t k_min, int32_t* tok, int32_t* blk,
+                        int32_t* committed_idx, int32_t* committed_rp, uint8_t* flags, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (!base_shape_ok(shape) || !logits || !tok || !blk || !committed_idx || !committed_rp ||
+      !flags || shape->V <= 0 || prompt_len < 0 || prompt_len > shape->S || block_len < 1 ||
+      k_min < 0 || tau != tau || !aligned16(logits))
+    return DLLM_ERR_INVALID_ARG;
+  if (block_len > kMaxBlockLen || shape->V % 8 != 0 || shape->V > 0x7fffffffL)
+    return DLLM_ERR_UNSUPPORTED;
+  dllm_status st = ws_status(ws, ws_bytes, dllm_workspace_bytes(DLLM_OP_COMMIT, shape, block_len));
+  if (st != DLLM_OK) return st;
+  CommitArgs c;
+  c.logits = logits;
+  c.B = shape->B; c.S = shape->S; c.V = shape->V;
+  c.P = prompt_len; c.L = block_len;
+  c.nblk = (shape->S - prompt_len + block_len - 1) / block_len;
+  c.tau = tau; c.k_min = k_min;
+  c.tok = tok; c.blk = blk; c.cidx = committed_idx; c.crp = committed_rp; c.flags = flags;
+  const size_t half = (((size_t)shape->B * block_len * 4) + 255) & ~(size_t)255;
+  c.conf = (float*)ws;
+  c.arg = (int32_t*)((char*)ws + half);
+  return hip_status(launch_commit(shape->dtype == DLLM_BF16, c, (hipStream_t)stream));
+}
+
+dllm_status dllm_embed_rows(const dllm_shape* shape, const void* emb, const void* mask_emb,
+                            const int32_t* tok, const int32_t* sel_idx, const int32_t* row_ptr,
+                            int32_t m_cap, void* x, void* stream) {
+  if (!base_shape_ok(shape) || !emb || !mask_emb || !tok || !sel_idx || !row_ptr || !x ||
+      shape->V <= 0 || m_cap < 0 || (long)m_cap > (long)shape->B * shape->S)
+    return DLLM_ERR_INVALID_ARG;
+  for (const void* p : {emb, mask_emb, (const void*)x})
+    if (!aligned16(p)) return DLLM_ERR_INVALID_ARG;
+  const size_t row_bytes = (size_t)shape->d * (shape->dtype == DLLM_BF16 ? 2 : 4);
+  if (row_bytes % 16 != 0) return DLLM_ERR_UNSUPPORTED;
+  return hip_status(launch_embed_rows(shape->B, m_cap, shape->V, row_bytes, emb, mask_emb, tok,
+                                      sel_idx, row_ptr, x, (hipStream_t)stream));
+}
 }  // extern "C"

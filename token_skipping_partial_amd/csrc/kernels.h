@@ -101,4 +101,26 @@ constexpr int kSalientMaxS = 8192;  // sequence length limit of the stable-token
 hipError_t launch_gather_rows(int B, int m_cap, size_t row_bytes, const void* src,
                               const int32_t* sel_idx, const int32_t* row_ptr, void* dst,
                               hipStream_t st);
+
+// ---- decode loop (decode.hip)
+constexpr int kMaxBlockLen = 256;  // one workgroup of the decision kernel holds a block
+struct CommitArgs {
+  const void* logits;  // [B, S, V]
+  int B, S;
+  long V;
+  int P, L, nblk;      // prompt length, block length, number of blocks
+  float tau;
+  int k_min;
+  int32_t* tok;        // [B, S], -1 = masked
+  int32_t* blk;        // [B] active block (nblk = done)
+  int32_t* cidx;       // [B * L] committed positions (flat ids)
+  int32_t* crp;        // [B + 1]
+  uint8_t* flags;      // [B, S] next step's selection flags (1 = active block)
+  float* conf;         // workspace [B, L]
+  int32_t* arg;        // workspace [B, L]
+};
+hipError_t launch_commit(bool bf16, const CommitArgs& c, hipStream_t st);
+hipError_t launch_embed_rows(int B, int m_cap, long V, size_t row_bytes, const void* emb,
+                             const void* mask_emb, const int32_t* tok, const int32_t* sel,
+                             const int32_t* rp, void* x, hipStream_t st);
 }  // namespace dllm

@@ -18,10 +18,10 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import (DELTA_COS, DELTA_L1N, OP_ATTN, OP_FFN, OP_QKV, SEL_THRESHOLD, SEL_TOPK, Shape,
-               dllm_gather_ffn_scatter, dllm_gather_kv_rows, dllm_gather_qkv_scatter_kv,
-               dllm_gather_rows, dllm_partial_attn, dllm_saliency, dllm_salient_attn,
-               dllm_select_compact, workspace)
+from . import (DELTA_COS, DELTA_L1N, OP_ATTN, OP_COMMIT, OP_FFN, OP_QKV, SEL_THRESHOLD, SEL_TOPK,
+               Shape, dllm_commit, dllm_embed_rows, dllm_gather_ffn_scatter, dllm_gather_kv_rows,
+               dllm_gather_qkv_scatter_kv, dllm_gather_rows, dllm_partial_attn, dllm_saliency,
+               dllm_salient_attn, dllm_select_compact, workspace)
 
 
 @dataclass
@@ -329,3 +329,77 @@ class LayerAdaptiveModel:
                 self._counts_evt.record()
                 self._counts_kind = inject
         return self.sel, self.rp
+
+
+class BlockDecoder:
+    """Semi-autoregressive block decoding that stays on the device: the early-skip step
+    (ES-dLLM, German summary page §2.B) with the active block forced into the selection, then the
+    commit of the active block from this step's logits (SlowFast, German summary page,
+    "Der SlowFast-Algorithmus" item 2: threshold commit, top-k update when too few pass; block
+    advance) and the embeddings of the committed tokens written into the next step's input.
+
+    Token ids, block indices, the selection flags and the input rows live on the device and are
+    updated by the library calls, so `step` never waits for the device and can be captured in a
+    HIP graph (`capture`) and replayed. `refresh` is the periodic full refresh: every layer on
+    every token (the caches and the skip-layer reference rebuilt from the current input).
+
+    model: EarlySkipModel whose m_cap covers B x (top-k + one block); emb [V, d] and mask_emb
+    [d] in the model's dtype; the model's shape carries V (the logits' vocabulary).
+    """
+
+    def __init__(self, model, emb, mask_emb, prompt_len: int, block_len: int, tau: float,
+                 k_min: int, device="cuda"):
+        sh = model.shape
+        if emb.shape != (sh.V, sh.d):
+            raise ValueError(f"embedding table {tuple(emb.shape)} is not [V={sh.V}, d={sh.d}]")
+        if model.m_cap < sh.B * (model.sel.k + block_len):
+            raise ValueError("the model's m_cap must hold, per sequence, the top-k plus one "
+                             "forced block")
+        self.model, self.emb, self.mask_emb = model, emb, mask_emb
+        self.P, self.L, self.tau, self.k_min = int(prompt_len), int(block_len), tau, int(k_min)
+        B, S = sh.B, sh.S
+        self.nblk = -(-(S - self.P) // self.L)
+        self.tok = torch.full((B, S), -1, dtype=torch.int32, device=device)
+        self.blk = torch.zeros(B, dtype=torch.int32, device=device)
+        self.flags = torch.zeros(B, S, dtype=torch.uint8, device=device)
+        self.cidx = torch.zeros(B * self.L, dtype=torch.int32, device=device)
+        self.crp = torch.zeros(B + 1, dtype=torch.int32, device=device)
+        self.ws = workspace(OP_COMMIT, sh, self.L, device)
+        self.x = torch.zeros(B, S, sh.d, dtype=sh.torch_dtype, device=device)
+        self.all_sel, self.all_rp = all_rows(sh, device)
+
+    def start(self, prompt, stream=None):
+        """prompt: int32 [B, P] token ids. Every later position is masked; block 0 is active."""
+        sh = self.model.shape
+        self.tok.fill_(-1)
+        self.tok[:, :self.P] = prompt
+        self.blk.zero_()
+        self.flags.zero_()
+        if self.nblk > 0:
+            self.flags[:, self.P:min(sh.S, self.P + self.L)] = 1
+        dllm_embed_rows(sh, self.emb, self.mask_emb, self.tok, self.all_sel, self.all_rp,
+                        sh.B * sh.S, self.x, stream)
+        self.model.fill(self.x, stream)
+
+    def step(self, logits, stream=None):
+        """One decoding step; `logits` [B, S, V] stand for this step's output of the model."""
+        sh = self.model.shape
+        self.model.step(self.x, force=self.flags, stream=stream)
+        dllm_commit(sh, logits, self.P, self.L, self.tau, self.k_min, self.tok, self.blk,
+                    self.cidx, self.crp, self.flags, self.ws, stream)
+        dllm_embed_rows(sh, self.emb, self.mask_emb, self.tok, self.cidx, self.crp,
+                        sh.B * self.L, self.x, stream)
+
+    def refresh(self, stream=None):
+        self.model.fill(self.x, stream)
+
+    def capture(self, logits):
+        """A HIP graph of one `step` reading `logits` (replay with .replay())."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                self.step(logits)
+        torch.cuda.current_stream().wait_stream(side)
+        return g
