@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llada_layer",
                    choices=["llada_layer", "llada_step", "llada_context", "llada_adaptive",
-                            "llada_response"],
+                            "llada_response", "llada_decode"],
                    help="llada_layer: one LLaDA-8B-shaped layer, B=1 (default); llada_step: the "
                         "full 32-layer early-skip step, B=8, S=1024, top-205 per sequence; "
                         "llada_context: the llada_layer step keeping the attention context of "
@@ -49,7 +49,11 @@ def parse():
                         "llada_adaptive: 32 LLaDA-8B layers, B=1, S=1024, per-layer FFN rows chosen "
                         "by the cosine change of every token's attention context; "
                         "llada_response: llada_adaptive with a 512-token prompt left out of "
-                        "response-only steps and re-injected every --inject-every steps")
+                        "response-only steps and re-injected every --inject-every steps; "
+                        "llada_decode: long-context block decoding (S=4096, 3584 prompt + 16 "
+                        "blocks of 32, 32 layers, early skip at layer 4, top-64 + the active "
+                        "block), commit at confidence 0.9 with a top-1 fallback, every step "
+                        "replayed from a HIP graph")
     p.add_argument("--inject-every", type=int, default=8,
                    help="llada_response: every n-th step re-injects the prompt")
     p.add_argument("--sets", type=int, default=16, help="rotated input/weight sets")
@@ -111,6 +115,9 @@ def main():
         return
     if args.workload == "llada_context":
         run_llada_context(args)
+        return
+    if args.workload == "llada_decode":
+        run_llada_decode(args)
         return
     if args.workload in ("llada_adaptive", "llada_response"):
         run_llada_adaptive(args, response=args.workload == "llada_response")
@@ -317,6 +324,91 @@ def run_llada_step(args):
         "config": {"workload": "llada_step: 32 LLaDA-8B-shaped layers, B=8, S=1024, early skip at "
                                "layer 4, alpha=0.5, top-205 per sequence",
                    "units_per_step": units, "selected_per_step": M},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_llada_decode(args):
+    """Long-context semi-autoregressive block decoding, B=1, S=4096 (3584 prompt + 16 blocks of
+    32), 32 LLaDA-8B layers: every step is the early-skip step (layers 0-3 on every token, L1
+    change of the layer-4 input ranks the rest, alpha 0: top-64 + the active block forced), the
+    commit of the active block (confidence > 0.9, else the best one) from that step's logits, and
+    the embeddings of the committed tokens; all on the device, replayed from one HIP graph per
+    logits buffer (4 rotating N(0, 3^2) buffers in which 10% of the rows carry one logit raised by
+    30, confidence ~1). Token and embedding tables are random."""
+    import synth
+    import token_skipping_partial_amd as tsp
+    from synth import workloads as W
+    from token_skipping_partial_amd.step import (BlockDecoder, EarlySkipModel, LayerWeights,
+                                                 SelectConfig)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dims, L, skip, k_sel, P, blk_len = W.LLADA_LONG, 32, 4, 64, 3584, 32
+    shape = tsp.Shape(B=dims.B, S=dims.S, d=dims.d, H=dims.H, Hkv=dims.Hkv, hd=dims.hd,
+                      F=dims.F, dtype="bf16", V=dims.V)
+    print(f"[bench] llada_decode: {L} layers of {shape}", file=sys.stderr, flush=True)
+    layers = [LayerWeights.from_dict(synth.layer_weights(dims.d, dims.H, dims.Hkv, dims.hd, dims.F,
+                                                         seed=7000 + l, device="cuda"))
+              for l in range(L)]
+    model = EarlySkipModel(shape, layers, skip, SelectConfig(mode=tsp.SEL_TOPK, k=k_sel, alpha=0.0),
+                           m_cap=dims.B * (k_sel + blk_len))
+    emb = synth.normal((dims.V, dims.d), 1.0, 7900, torch.bfloat16, "cuda")
+    mask = synth.normal((dims.d,), 1.0, 7901, torch.bfloat16, "cuda")
+    dec = BlockDecoder(model, emb, mask, P, blk_len, 0.9, 1)
+    bufs = []
+    for i in range(4):
+        z = synth.normal((dims.B, dims.S, dims.V), 3.0, 7800 + i, torch.float32, "cuda")
+        rows = synth.large_positions(dims.B, dims.S, dims.S // 10, seed=7850 + i, device="cuda")
+        g = torch.Generator(device="cuda").manual_seed(7860 + i)
+        idx = torch.randint(0, dims.V, (dims.B, dims.S), generator=g, device="cuda")
+        z.view(-1, dims.V)[torch.arange(dims.B * dims.S, device="cuda"),
+                           idx.view(-1)] += 30.0 * rows.view(-1).float()
+        bufs.append(z.to(torch.bfloat16))
+        del z
+    prompt = torch.randint(0, dims.V, (dims.B, P), generator=torch.Generator().manual_seed(7870),
+                           dtype=torch.int32).cuda()
+    dec.start(prompt)
+    torch.cuda.synchronize()
+    graphs = [dec.capture(b) for b in bufs]
+    for t in range(args.warmup):
+        graphs[t % 4].replay()
+    torch.cuda.synchronize()
+    tok0 = int(dec.tok.ge(0).sum().item())
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    counts = torch.zeros(args.steps, dtype=torch.int32, device="cuda")
+    t0.record(stream)
+    for t in range(args.steps):
+        graphs[(args.warmup + t) % 4].replay()
+        counts[t] = model.step1.row_ptr[-1]
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    M = float(counts.float().mean().item())
+    committed = int(dec.tok.ge(0).sum().item()) - tok0
+    # one periodic full refresh (every layer on every token), timed on its own
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    dec.refresh()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    units = skip * dims.B * dims.S + (L - skip) * M
+    out = {
+        "metric": METRIC, "value": round(units / (ms * 1e-3), 1),
+        "unit": "selected-token layer-steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: random token ids and embedding table N(0,1); logits N(0,3^2) with "
+                "10% of rows spiked by +30 on one logit; random-init weights N(0,0.02^2)",
+        "config": {"workload": "llada_decode: B=1, S=4096 (3584 prompt + 16 blocks of 32), 32 "
+                               "LLaDA-8B-shaped layers, early skip at layer 4, top-64 by delta + "
+                               "the active block, commit at confidence 0.9 with a top-1 fallback, "
+                               "steps replayed from HIP graphs",
+                   "units_per_step": units, "selected_per_step": M,
+                   "tokens_committed": committed,
+                   "tokens_per_s": round(committed / (ms * 1e-3 * args.steps), 1),
+                   "blocks_done": int(dec.blk[0].item()),
+                   "refresh_ms": round(r0.elapsed_time(r1), 3)},
     }
     print(json.dumps(out), flush=True)
 
