@@ -6,6 +6,7 @@
  *
  *   dllm_saliency               per-token importance score
  *   dllm_select_compact         top-k or threshold selection + stream compaction
+ *   (dllm_flags_from_rows       restricts a later selection to the rows of an earlier one)
  *   dllm_gather_qkv_scatter_kv  QKV projection of the selected tokens, K/V scattered into the cache
  *   dllm_partial_attn           selected queries against the whole (updated) K/V cache, no mask
  *   dllm_gather_ffn_scatter     output projection + SwiGLU FFN of the selected tokens, scattered
@@ -114,9 +115,12 @@ typedef struct {
  *   c     = max_v softmax(logits[b,s,:])  (largest probability at temperature 1, previous step)
  *   delta = variation of h_cur[b,s,:] against h_prev[b,s,:] of kind `delta_kind`.
  * h_cur, h_prev : [B,S,d] dtype; may be NULL only when alpha == 1. d % 8 == 0.
- * logits        : [B,S,V] dtype; may be NULL only when alpha == 0.
+ * logits        : [B,S,V] dtype, or NULL: then c is read from conf_out (required when alpha != 0
+ *                 without logits, together with h_cur/h_prev), the confidence an earlier call
+ *                 wrote from the same logits [ES-dLLM §2.B second skip point: the score of a later
+ *                 layer reuses the previous step's confidence].
  * score         : [B,S] float32 (required).
- * conf_out      : [B,S] float32 or NULL (requires logits).
+ * conf_out      : [B,S] float32 or NULL: with logits, c is written there; without, see above.
  * delta_out     : [B,S] float32 or NULL (requires h_cur/h_prev).
  * alpha in [0,1]. With alpha == 0 and conf_out == NULL the logits are not read.
  * Workspace: none. */
@@ -142,6 +146,15 @@ dllm_status dllm_select_compact(const dllm_shape* shape, int32_t mode, float tau
                                 const float* score, const uint8_t* force,
                                 int32_t* sel_idx, int32_t* row_ptr,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* Flags that restrict a later selection to listed rows [ES-dLLM §2.B: a second skip point
+ * deeper in the model ranks only the tokens still being computed]. flags[p] = 2 (excluded) for
+ * every position p = b*S + s, then for j < M = min(row_ptr[B], m_cap), p = sel_idx[j]:
+ * flags[p] = force[p] & 1 (forced stays forced; NULL force: 0, a candidate). force and flags
+ * are [B,S] uint8 and must not be the same array. Workspace: none. */
+dllm_status dllm_flags_from_rows(const dllm_shape* shape, const uint8_t* force,
+                                 const int32_t* sel_idx, const int32_t* row_ptr, int32_t m_cap,
+                                 uint8_t* flags, void* stream);
 
 /* (3) Gathered QKV projection + K/V cache scatter [ES-dLLM §2.B partial cache update].
  * For j < M = min(row_ptr[B], m_cap), with (b, s) = (sel_idx[j] / S, sel_idx[j] % S):

@@ -111,13 +111,18 @@ def max_softmax_confidence(logits: np.ndarray) -> np.ndarray:
     return 1.0 / np.sum(np.exp(z - m), axis=-1)
 
 
-def saliency(h_cur, h_prev, logits, alpha: float, kind: int = DELTA_L1N):
+def saliency(h_cur, h_prev, logits, alpha: float, kind: int = DELTA_L1N, conf=None):
     """Importance score per token, ES-dLLM (German page) §2.A equation.
 
-    h_cur, h_prev: [..., d] (may be None when alpha == 1); logits: [..., V] (None when alpha == 0).
+    h_cur, h_prev: [..., d] (may be None when alpha == 1); logits: [..., V] (None when alpha == 0,
+    or when `conf`, the confidence of the same logits computed earlier, is given: the score at a
+    second skip point, §2.B, reuses the previous step's confidence).
     Returns (score float32 [...], conf float64 [...] or None, delta float64 [...] or None).
     """
-    conf = max_softmax_confidence(logits) if logits is not None else None
+    if logits is not None:
+        conf = max_softmax_confidence(logits)
+    elif conf is not None:
+        conf = np.asarray(conf, dtype=np.float64)
     delta = delta_variation(h_cur, h_prev, kind) if h_cur is not None else None
     c = conf if conf is not None else 0.0
     v = delta if delta is not None else 0.0
@@ -415,11 +420,11 @@ def commit_step(logits, tok, blk, prompt_len: int, block_len: int, tau: float, k
     number of blocks, which means done). The next step's selection flags force the positions of
     the (possibly new) active block.
 
-    logits [B, S, V]; tok int [B, S] (-1 = masked); blk int [B].
+    logits [B, S, V] (anything indexable as logits[b, s] -> a row; only active-block rows are
+    read); tok int [B, S] (-1 = masked); blk int [B].
     Returns (tok', blk', committed ids (flat b S + s, ascending per sequence), row_ptr,
              flags uint8 [B, S]).
     """
-    logits = np.asarray(logits)
     tok = np.array(tok, dtype=np.int64, copy=True)
     blk = np.array(blk, dtype=np.int64, copy=True)
     B, S = tok.shape
@@ -462,3 +467,15 @@ def embed_rows(emb, mask_emb, tok, sel_idx, row_ptr, x):
         t = int(tok[b, s])
         x[b, s] = np.asarray(emb[t] if t >= 0 else mask_emb, dtype=np.float64)
     return x
+
+
+def flags_from_rows(force, sel_idx, row_ptr, B: int, S: int):
+    """Selection flags that restrict a later selection to the listed rows (ES-dLLM, German
+    summary page §2.B: the second skip point ranks only the tokens still being computed): a
+    listed position is a candidate, or forced if bit 0 of its `force` flag is set; every other
+    position is excluded (flag 2)."""
+    flags = np.full((B, S), 2, dtype=np.uint8)
+    for flat in np.asarray(sel_idx[:int(row_ptr[-1])], dtype=np.int64):
+        b, s = int(flat) // S, int(flat) % S
+        flags[b, s] = (int(force[b, s]) & 1) if force is not None else 0
+    return flags

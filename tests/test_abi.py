@@ -101,6 +101,7 @@ def test_saliency_validation():
     assert rc(f, s, 0, 0.5, P, P, P, None) == tsp.DLLM_ERR_INVALID_ARG      # no score
     assert rc(f, s, 0, 0.5, P, None, P, P) == tsp.DLLM_ERR_INVALID_ARG      # h_prev missing
     assert rc(f, s, 0, 0.0, P, P, None, P, P) == tsp.DLLM_ERR_INVALID_ARG   # conf_out w/o logits
+    assert rc(f, s, 0, 0.5, None, None, None, P, P) == tsp.DLLM_ERR_INVALID_ARG  # conf in, no h
     assert rc(f, s, 0, 0.5, P + 2, P, P, P) == tsp.DLLM_ERR_INVALID_ARG     # misaligned
     bad = llada(); bad.V = 1001
     assert rc(f, bad, 0, 0.5, P, P, P, P) == tsp.DLLM_ERR_UNSUPPORTED      # V % 8

@@ -663,3 +663,25 @@ def test_embed_rows_copies_the_listed_rows():
     y = O.embed_rows(emb, mask, tok, np.array([1, 2], np.int32), np.array([0, 2], np.int32), x)
     assert np.array_equal(y[0, 1], mask) and np.array_equal(y[0, 2], emb[6])
     assert np.array_equal(y[0, 0], x[0, 0]) and np.array_equal(y[0, 3], x[0, 3])
+
+
+def test_saliency_with_earlier_confidence_equals_the_logits_path():
+    """A second skip point reuses the previous step's confidence: the score from the stored
+    confidence equals the score computed from the logits themselves."""
+    rng = np.random.default_rng(5)
+    h1, h0 = rng.standard_normal((2, 6, 16)), rng.standard_normal((2, 6, 16))
+    z = rng.normal(0, 3, (2, 6, 40))
+    s_a, conf, _ = O.saliency(h1, h0, z, 0.5)
+    s_b, conf_b, _ = O.saliency(h1, h0, None, 0.5, conf=conf)
+    assert np.array_equal(s_a, s_b) and np.array_equal(conf, conf_b)
+    s_c, _, d = O.saliency(h1, h0, None, 0.0)
+    assert np.array_equal(s_c, d.astype(np.float32))
+
+
+def test_flags_from_rows_restrict_to_the_listed_rows():
+    force = np.array([[3, 0, 1, 0], [0, 2, 0, 1]], np.uint8)
+    sel = np.array([0, 1, 5, 7], np.int32)
+    rp = np.array([0, 2, 4], np.int32)
+    f = O.flags_from_rows(force, sel, rp, 2, 4)
+    assert f.tolist() == [[1, 0, 2, 2], [2, 0, 2, 1]]
+    assert O.flags_from_rows(None, sel, rp, 2, 4).tolist() == [[0, 0, 2, 2], [2, 0, 2, 0]]

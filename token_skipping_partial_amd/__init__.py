@@ -30,6 +30,7 @@ MAX_BLOCK_LEN = 256
 EXPORTS = ("dllm_saliency", "dllm_select_compact", "dllm_gather_qkv_scatter_kv",
            "dllm_partial_attn", "dllm_gather_ffn_scatter", "dllm_gather_kv_rows",
            "dllm_salient_attn", "dllm_gather_rows", "dllm_commit", "dllm_embed_rows",
+           "dllm_flags_from_rows",
            "dllm_workspace_bytes", "dllm_status_string", "dllm_version")
 
 
@@ -89,6 +90,7 @@ def _load():
         "dllm_gather_rows": (I32, [SP, P, I32, P, P, I32, P, P]),
         "dllm_commit": (I32, [SP, P, I32, I32, F, I32, P, P, P, P, P, P, SZ, P]),
         "dllm_embed_rows": (I32, [SP, P, P, P, P, P, I32, P, P]),
+        "dllm_flags_from_rows": (I32, [SP, P, P, P, I32, P, P]),
         "dllm_workspace_bytes": (SZ, [I32, SP, I32]),
         "dllm_status_string": (ctypes.c_char_p, [I32]),
         "dllm_version": (I32, []),
@@ -234,3 +236,9 @@ def dllm_embed_rows(shape, emb, mask_emb, tok, sel_idx, row_ptr, m_cap, x, strea
     _check(_lib.dllm_embed_rows(ctypes.byref(shape), _ptr(emb), _ptr(mask_emb), _ptr(tok),
                                 _ptr(sel_idx), _ptr(row_ptr), int(m_cap), _ptr(x),
                                 _stream(stream)), "dllm_embed_rows")
+
+
+def dllm_flags_from_rows(shape, force, sel_idx, row_ptr, m_cap, flags, stream=None):
+    _check(_lib.dllm_flags_from_rows(ctypes.byref(shape), _ptr(force), _ptr(sel_idx),
+                                     _ptr(row_ptr), int(m_cap), _ptr(flags), _stream(stream)),
+           "dllm_flags_from_rows")

@@ -111,8 +111,10 @@ dllm_status dllm_saliency(const dllm_shape* shape, int32_t delta_kind, float alp
   const bool has_h = h_cur != nullptr || h_prev != nullptr;
   if (has_h && (!h_cur || !h_prev)) return DLLM_ERR_INVALID_ARG;
   if (alpha != 1.f && !has_h) return DLLM_ERR_INVALID_ARG;
-  if (alpha != 0.f && !logits) return DLLM_ERR_INVALID_ARG;
-  if (conf_out && !logits) return DLLM_ERR_INVALID_ARG;
+  // without logits, `conf_out` is the confidence input of the alpha term (an earlier call's output)
+  const bool conf_in = !logits && alpha != 0.f;
+  if (conf_in && (!conf_out || !has_h)) return DLLM_ERR_INVALID_ARG;
+  if (conf_out && !logits && !conf_in) return DLLM_ERR_INVALID_ARG;
   if (delta_out && !has_h) return DLLM_ERR_INVALID_ARG;
   if (logits && shape->V <= 0) return DLLM_ERR_INVALID_ARG;
   for (const void* p : {h_cur, h_prev, logits, (const void*)score, (const void*)conf_out,
@@ -134,7 +136,8 @@ dllm_status dllm_saliency(const dllm_shape* shape, int32_t delta_kind, float alp
   // the vocabulary stream is skipped when neither the score nor an output needs it
   a.logits = (alpha != 0.f || conf_out) ? logits : nullptr;
   a.score = score;
-  a.conf_out = conf_out;
+  a.conf_out = logits ? conf_out : nullptr;
+  a.conf_in = conf_in ? conf_out : nullptr;
   a.delta_out = delta_out;
   return hip_status(launch_saliency(a, shape->dtype == DLLM_BF16, (hipStream_t)stream));
 }
@@ -313,4 +316,14 @@ dllm_status dllm_embed_rows(const dllm_shape* shape, const void* emb, const void
   return hip_status(launch_embed_rows(shape->B, m_cap, shape->V, row_bytes, emb, mask_emb, tok,
                                       sel_idx, row_ptr, x, (hipStream_t)stream));
 }
+dllm_status dllm_flags_from_rows(const dllm_shape* shape, const uint8_t* force,
+                                 const int32_t* sel_idx, const int32_t* row_ptr, int32_t m_cap,
+                                 uint8_t* flags, void* stream) {
+  if (!base_shape_ok(shape) || !sel_idx || !row_ptr || !flags || m_cap < 0 ||
+      (long)m_cap > (long)shape->B * shape->S || (force && (const void*)force == (void*)flags))
+    return DLLM_ERR_INVALID_ARG;
+  return hip_status(launch_flags_from_rows(shape->B, shape->S, force, sel_idx, row_ptr, m_cap,
+                                           flags, (hipStream_t)stream));
+}
+
 }  // extern "C"

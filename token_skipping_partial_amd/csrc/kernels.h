@@ -18,6 +18,7 @@ struct SaliencyArgs {
   float* score;
   float* conf_out;
   float* delta_out;
+  const float* conf_in;  // no logits, alpha != 0: the confidence of an earlier call
 };
 hipError_t launch_saliency(const SaliencyArgs& a, bool bf16, hipStream_t st);
 
@@ -30,6 +31,8 @@ struct SelectArgs {
   int32_t* row_ptr;
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+hipError_t launch_flags_from_rows(int B, int S, const uint8_t* force, const int32_t* sel,
+                                  const int32_t* rp, int m_cap, uint8_t* flags, hipStream_t st);
 
 // ---------------------------------------------------------------- gathered projections
 struct ProjShape {

@@ -175,7 +175,9 @@ __global__ __launch_bounds__(256) void saliency_hidden_kernel(SaliencyArgs a) {
   wave_sums(hs);
   if (lane == 0) {
     float var = variation(hs, a.kind, a.d);
-    a.score[tok] = (1.0f - a.alpha) * var;  // alpha * confidence is not requested (alpha == 0)
+    // the confidence term comes from an earlier call on the same logits, or is off (alpha == 0)
+    a.score[tok] = a.conf_in ? a.alpha * a.conf_in[tok] + (1.0f - a.alpha) * var
+                             : (1.0f - a.alpha) * var;
     if (a.delta_out) a.delta_out[tok] = var;
   }
 }

@@ -191,6 +191,34 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   }
 }
 
+// flags restricting a later selection to listed rows: every position excluded (2), then the
+// listed ones candidates (0) or forced (1) as bit 0 of `force` says
+__global__ __launch_bounds__(256) void flags_fill_kernel(uint8_t* flags, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) flags[i] = 2;
+}
+__global__ __launch_bounds__(256) void flags_rows_kernel(const uint8_t* force, const int32_t* sel,
+                                                         const int32_t* rp, int B, int m_cap,
+                                                         uint8_t* flags) {
+  const int M = min(rp[B], m_cap);
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= M) return;
+  const int p = sel[j];
+  flags[p] = force ? (uint8_t)(force[p] & 1) : (uint8_t)0;
+}
+
+hipError_t launch_flags_from_rows(int B, int S, const uint8_t* force, const int32_t* sel,
+                                  const int32_t* rp, int m_cap, uint8_t* flags, hipStream_t st) {
+  const size_t n = (size_t)B * S;
+  hipLaunchKernelGGL(flags_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, flags,
+                     n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || m_cap == 0) return e;
+  hipLaunchKernelGGL(flags_rows_kernel, dim3((unsigned)((m_cap + 255) / 256)), dim3(256), 0, st,
+                     force, sel, rp, B, m_cap, flags);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   size_t lds = (size_t)a.S * 4 + (((size_t)a.S + 3) & ~(size_t)3);
   hipLaunchKernelGGL(select_kernel, dim3(a.B), dim3(kSelThreads), lds, st, a);

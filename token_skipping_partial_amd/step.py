@@ -19,7 +19,8 @@ from dataclasses import dataclass, field
 import torch
 
 from . import (DELTA_COS, DELTA_L1N, OP_ATTN, OP_COMMIT, OP_FFN, OP_QKV, SEL_THRESHOLD, SEL_TOPK,
-               Shape, dllm_commit, dllm_embed_rows, dllm_gather_ffn_scatter, dllm_gather_kv_rows,
+               Shape, dllm_commit, dllm_embed_rows, dllm_flags_from_rows, dllm_gather_ffn_scatter,
+               dllm_gather_kv_rows,
                dllm_gather_qkv_scatter_kv, dllm_gather_rows, dllm_partial_attn, dllm_saliency,
                dllm_salient_attn, dllm_select_compact, workspace)
 
@@ -109,10 +110,12 @@ class SingleLayerStep:
         self.row_ptr = torch.empty(B + 1, dtype=torch.int32, device=device)
         self.scratch = LayerScratch(shape, m_cap, device)
 
-    def score_and_select(self, h_cur, h_prev, logits, force=None, stream=None):
+    def score_and_select(self, h_cur, h_prev, logits, force=None, stream=None, conf=None):
+        """conf: [B, S] float32; with logits the confidence is also written there, without
+        logits (alpha != 0) it is read from there."""
         c = self.sel
         dllm_saliency(self.shape, c.delta_kind, c.alpha, h_cur, h_prev, logits, self.score,
-                      stream=stream)
+                      conf, stream=stream)
         dllm_select_compact(self.shape, c.mode, c.tau, c.k, self.score, force, self.sel_idx,
                             self.row_ptr, stream=stream)
 
@@ -129,10 +132,15 @@ class EarlySkipModel:
     hidden[l] is the input of layer l (hidden[0] = embeddings); layer l writes hidden[l + 1].
     Layers [0, skip) run on every token; the saliency of hidden[skip] against its value at the
     previous step picks the rows for layers [skip, L).
+
+    Optional second skip point (ES-dLLM German summary page §2.B names 1/8 and 1/4 of the depth):
+    at layer skip2 the rows of the first selection are ranked again by the same score on
+    hidden[skip2] (its change against the previous step, the confidence of the first stage reused)
+    and only the top-k2 of them (plus the forced ones) go on through layers [skip2, L).
     """
 
     def __init__(self, shape: Shape, layers: list, skip: int, sel: SelectConfig, m_cap: int,
-                 device="cuda"):
+                 device="cuda", skip2: int = 0, k2: int = 0):
         self.shape, self.layers, self.skip, self.sel, self.m_cap = shape, layers, skip, sel, m_cap
         B, S, d, Hkv, hd = shape.B, shape.S, shape.d, shape.Hkv, shape.hd
         dt = shape.torch_dtype
@@ -145,6 +153,17 @@ class EarlySkipModel:
         self.dense = LayerScratch(shape, B * S, device)
         self.step1 = SingleLayerStep(shape, sel, m_cap, device)  # score/select buffers
         self.sparse = self.step1.scratch
+        if skip2 and not skip < skip2 < L:
+            raise ValueError(f"second skip point {skip2} not inside ({skip}, {L})")
+        self.skip2, self.k2 = int(skip2), int(k2)
+        self.conf = torch.zeros(B, shape.S, dtype=torch.float32, device=device)
+        if self.skip2:
+            self.h_ref2 = torch.zeros(B, shape.S, d, dtype=dt, device=device)
+            self.flags2 = torch.zeros(B, shape.S, dtype=torch.uint8, device=device)
+            self.step2 = SingleLayerStep(shape, SelectConfig(mode=SEL_TOPK, k=self.k2,
+                                                             alpha=sel.alpha,
+                                                             delta_kind=sel.delta_kind),
+                                         m_cap, device)
 
     def fill(self, x0, stream=None):
         """Step 0: every layer on every token; primes caches and the skip-layer reference."""
@@ -153,19 +172,36 @@ class EarlySkipModel:
             selected_layer(self.shape, w, self.hidden[l], self.k[l], self.v[l], self.hidden[l + 1],
                            self.all_sel, self.all_rp, self.dense, stream)
         self.h_ref.copy_(self.hidden[self.skip])
+        if self.skip2:
+            self.h_ref2.copy_(self.hidden[self.skip2])
 
     def step(self, x, logits=None, force=None, stream=None):
+        """Returns the rows of the last layers: the first selection's, or with a second skip point
+        the second one's (the first is in step1.sel_idx / step1.row_ptr)."""
         self.hidden[0].copy_(x)
         for l in range(self.skip):
             selected_layer(self.shape, self.layers[l], self.hidden[l], self.k[l], self.v[l],
                            self.hidden[l + 1], self.all_sel, self.all_rp, self.dense, stream)
         s = self.step1
-        s.score_and_select(self.hidden[self.skip], self.h_ref, logits, force, stream)
+        s.score_and_select(self.hidden[self.skip], self.h_ref, logits, force, stream,
+                           conf=self.conf if (self.skip2 and logits is not None) else None)
         self.h_ref.copy_(self.hidden[self.skip])
-        for l in range(self.skip, len(self.layers)):
+        last = self.skip2 or len(self.layers)
+        for l in range(self.skip, last):
             selected_layer(self.shape, self.layers[l], self.hidden[l], self.k[l], self.v[l],
                            self.hidden[l + 1], s.sel_idx, s.row_ptr, self.sparse, stream)
-        return s.sel_idx, s.row_ptr
+        if not self.skip2:
+            return s.sel_idx, s.row_ptr
+        s2 = self.step2
+        dllm_flags_from_rows(self.shape, force, s.sel_idx, s.row_ptr, self.m_cap, self.flags2,
+                             stream)
+        s2.score_and_select(self.hidden[self.skip2], self.h_ref2, None, self.flags2, stream,
+                            conf=self.conf if self.sel.alpha != 0.0 else None)
+        self.h_ref2.copy_(self.hidden[self.skip2])
+        for l in range(self.skip2, len(self.layers)):
+            selected_layer(self.shape, self.layers[l], self.hidden[l], self.k[l], self.v[l],
+                           self.hidden[l + 1], s2.sel_idx, s2.row_ptr, s2.scratch, stream)
+        return s2.sel_idx, s2.row_ptr
 
 
 class LayerAdaptiveModel:
