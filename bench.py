@@ -54,6 +54,12 @@ def parse():
                         "blocks of 32, 32 layers, early skip at layer 4, top-64 + the active "
                         "block), commit at confidence 0.9 with a top-1 fallback, every step "
                         "replayed from a HIP graph")
+    p.add_argument("--second-skip", type=int, default=0,
+                   help="llada_step: a second skip point at this layer (0 = none; the pages name "
+                        "1/8 and 1/4 of the depth: 4 and 8)")
+    p.add_argument("--second-k", type=int, default=0,
+                   help="llada_step: rows per sequence kept at the second skip point "
+                        "(0 = half of the first top-k)")
     p.add_argument("--inject-every", type=int, default=8,
                    help="llada_response: every n-th step re-injects the prompt")
     p.add_argument("--sets", type=int, default=16, help="rotated input/weight sets")
@@ -291,8 +297,9 @@ def run_llada_step(args):
     layers = [LayerWeights.from_dict(synth.layer_weights(dims.d, dims.H, dims.Hkv, dims.hd, dims.F,
                                                          seed=7000 + l, device="cuda"))
               for l in range(L)]
+    k2 = (args.second_k or k_sel // 2) if args.second_skip else 0
     model = EarlySkipModel(shape, layers, skip, SelectConfig(mode=tsp.SEL_TOPK, k=k_sel, alpha=0.5),
-                           m_cap=dims.B * k_sel)
+                           m_cap=dims.B * k_sel, skip2=args.second_skip, k2=k2)
     nsteps = args.warmup + args.steps
     xs = [synth.normal((dims.B, dims.S, dims.d), 1.0, 7500, torch.bfloat16, "cuda")]
     for t in range(1, nsteps + 1):
@@ -313,7 +320,9 @@ def run_llada_step(args):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
     M = int(model.step1.row_ptr[-1].item())
-    units = skip * dims.B * dims.S + (L - skip) * M
+    skip2 = args.second_skip or L
+    M2 = int(model.step2.row_ptr[-1].item()) if args.second_skip else M
+    units = skip * dims.B * dims.S + (skip2 - skip) * M + (L - skip2) * M2
     out = {
         "metric": METRIC, "value": round(units / (ms * 1e-3), 1),
         "unit": "selected-token layer-steps/s", "n_gpus": 1, "steps": args.steps,
@@ -325,6 +334,10 @@ def run_llada_step(args):
                                "layer 4, alpha=0.5, top-205 per sequence",
                    "units_per_step": units, "selected_per_step": M},
     }
+    if args.second_skip:
+        out["config"]["workload"] += (f", second skip point at layer {args.second_skip} keeping "
+                                      f"top-{k2} of those per sequence")
+        out["config"]["selected_after_second_skip"] = M2
     print(json.dumps(out), flush=True)
 
 

@@ -160,10 +160,12 @@ class EarlySkipModel:
         if self.skip2:
             self.h_ref2 = torch.zeros(B, shape.S, d, dtype=dt, device=device)
             self.flags2 = torch.zeros(B, shape.S, dtype=torch.uint8, device=device)
-            self.step2 = SingleLayerStep(shape, SelectConfig(mode=SEL_TOPK, k=self.k2,
-                                                             alpha=sel.alpha,
-                                                             delta_kind=sel.delta_kind),
-                                         m_cap, device)
+            # the second stage keeps top-k2 per sequence plus forced rows: its layers are planned
+            # for B * k2 rows (workspaces sized for any plan)
+            self.shape2 = shape.with_plan(max(1, min(m_cap, B * self.k2)))
+            self.step2 = SingleLayerStep(shape.with_plan(1), SelectConfig(
+                mode=SEL_TOPK, k=self.k2, alpha=sel.alpha, delta_kind=sel.delta_kind), m_cap,
+                device)
 
     def fill(self, x0, stream=None):
         """Step 0: every layer on every token; primes caches and the skip-layer reference."""
@@ -199,7 +201,7 @@ class EarlySkipModel:
                             conf=self.conf if self.sel.alpha != 0.0 else None)
         self.h_ref2.copy_(self.hidden[self.skip2])
         for l in range(self.skip2, len(self.layers)):
-            selected_layer(self.shape, self.layers[l], self.hidden[l], self.k[l], self.v[l],
+            selected_layer(self.shape2, self.layers[l], self.hidden[l], self.k[l], self.v[l],
                            self.hidden[l + 1], s2.sel_idx, s2.row_ptr, s2.scratch, stream)
         return s2.sel_idx, s2.row_ptr
 
