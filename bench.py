@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llada_layer",
                    choices=["llada_layer", "llada_step", "llada_context", "llada_adaptive",
-                            "llada_response", "llada_decode"],
+                            "llada_response", "llada_decode", "dream_sweep"],
                    help="llada_layer: one LLaDA-8B-shaped layer, B=1 (default); llada_step: the "
                         "full 32-layer early-skip step, B=8, S=1024, top-205 per sequence; "
                         "llada_context: the llada_layer step keeping the attention context of "
@@ -53,7 +53,9 @@ def parse():
                         "llada_decode: long-context block decoding (S=4096, 3584 prompt + 16 "
                         "blocks of 32, 32 layers, early skip at layer 4, top-64 + the active "
                         "block), commit at confidence 0.9 with a top-1 fallback, every step "
-                        "replayed from a HIP graph")
+                        "replayed from a HIP graph; dream_sweep: 28 Dream-7B-shaped layers (GQA "
+                        "28/4), B=16, S=2048, early skip at layer 4, top-k by delta at 1, 2, 5, 10, "
+                        "25 and 50%% of the tokens: step time and per-call rates")
     p.add_argument("--second-skip", type=int, default=0,
                    help="llada_step: a second skip point at this layer (0 = none; the pages name "
                         "1/8 and 1/4 of the depth: 4 and 8)")
@@ -124,6 +126,9 @@ def main():
         return
     if args.workload == "llada_decode":
         run_llada_decode(args)
+        return
+    if args.workload == "dream_sweep":
+        run_dream_sweep(args)
         return
     if args.workload in ("llada_adaptive", "llada_response"):
         run_llada_adaptive(args, response=args.workload == "llada_response")
@@ -422,6 +427,107 @@ def run_llada_decode(args):
                    "tokens_per_s": round(committed / (ms * 1e-3 * args.steps), 1),
                    "blocks_done": int(dec.blk[0].item()),
                    "refresh_ms": round(r0.elapsed_time(r1), 3)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_dream_sweep(args):
+    """28 Dream-7B-shaped layers (d 3584, 28 query / 4 kv heads x 128, FFN 18944), B=16, S=2048:
+    layers 0-3 on every token, the L1 change of the layer-4 input (alpha 0) picks the top-k of
+    every sequence for layers 4-27. For each selected fraction (1, 2, 5, 10, 25, 50%: the last
+    four are the workload's, the first two show where the products stop being bound by the
+    weight stream): a fill, then timed steps, and the three layer calls of one selected layer
+    timed one by one with their algorithmic flops and bytes. Inputs move by N(0, 0.5^2) at
+    exactly k tokens of every sequence per step, N(0, (1e-3)^2) elsewhere."""
+    import synth
+    import token_skipping_partial_amd as tsp
+    from synth import workloads as W
+    from token_skipping_partial_amd.step import EarlySkipModel, LayerWeights, SelectConfig
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dims, L, skip = W.DREAM_GQA, 28, 4
+    shape = tsp.Shape(B=dims.B, S=dims.S, d=dims.d, H=dims.H, Hkv=dims.Hkv, hd=dims.hd,
+                      F=dims.F, dtype="bf16", V=0)
+    print(f"[bench] dream_sweep: {L} layers of {shape}", file=sys.stderr, flush=True)
+    layers = [LayerWeights.from_dict(synth.layer_weights(dims.d, dims.H, dims.Hkv, dims.hd, dims.F,
+                                                         seed=8000 + l, device="cuda"))
+              for l in range(L)]
+    Nq, Nkv = dims.H * dims.hd, dims.Hkv * dims.hd
+    w_bytes = 2 * (dims.d * (Nq + 2 * Nkv) + dims.d * Nq + 3 * dims.d * dims.F)
+    stream = torch.cuda.current_stream()
+    steps = max(1, min(args.steps, 8))
+    points = []
+    x0 = synth.normal((dims.B, dims.S, dims.d), 1.0, 8500, torch.bfloat16, "cuda")
+    for frac in (0.01, 0.02, 0.05, 0.10, 0.25, 0.50):
+        k = max(1, round(frac * dims.S))
+        M = dims.B * k
+        model = EarlySkipModel(shape, layers, skip, SelectConfig(mode=tsp.SEL_TOPK, k=k, alpha=0.0),
+                               m_cap=M)
+        xs = [x0]
+        for t in range(1, 3 + steps + 1):
+            large = synth.large_positions(dims.B, dims.S, k, seed=8600 + t, device="cuda")
+            xs.append(synth.perturb(xs[-1], large, seed=8700 + t))
+        model.fill(xs[0])
+        for t in range(2):
+            model.step(xs[1 + t])
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for t in range(steps):
+            model.step(xs[3 + t])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        # the three calls of layer `skip` on this step's rows, one event pair each (3 repeats)
+        s1, sc, w = model.step1, model.sparse, layers[skip]
+        calls = {
+            "gather_qkv_scatter_kv": lambda: tsp.dllm_gather_qkv_scatter_kv(
+                shape, model.hidden[skip], w.g_attn, w.w_qkv, s1.sel_idx, s1.row_ptr, M, sc.q_sel,
+                model.k[skip], model.v[skip], sc.ws_qkv),
+            "partial_attn": lambda: tsp.dllm_partial_attn(
+                shape, 1.0 / math.sqrt(dims.hd), sc.q_sel, model.k[skip], model.v[skip],
+                s1.sel_idx, s1.row_ptr, M, sc.o_sel, sc.ws_attn),
+            "gather_ffn_scatter": lambda: tsp.dllm_gather_ffn_scatter(
+                shape, model.hidden[skip], sc.o_sel, w.w_o, w.g_ffn, w.w_gate, w.w_up, w.w_down,
+                s1.sel_idx, s1.row_ptr, M, model.hidden[skip + 1], sc.ws_ffn),
+        }
+        flops = {"gather_qkv_scatter_kv": 2.0 * M * dims.d * (Nq + 2 * Nkv),
+                 "partial_attn": 4.0 * M * dims.S * Nq,
+                 "gather_ffn_scatter": 2.0 * M * dims.d * (Nq + 3 * dims.F)}
+        nbytes = {"gather_qkv_scatter_kv": 2 * dims.d * (Nq + 2 * Nkv) + 2 * M * (dims.d + Nq + 2 * Nkv),
+                  "partial_attn": 2 * dims.B * dims.S * 2 * Nkv + 2 * M * 2 * Nq,
+                  "gather_ffn_scatter": 2 * dims.d * (Nq + 3 * dims.F) + 2 * M * (Nq + 3 * dims.d)}
+        per = {}
+        for name, fn in calls.items():
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(3):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / 3 * 1e3
+            per[name] = {"us": round(us, 1), "TFLOP/s": round(flops[name] / us / 1e6, 1),
+                         "GB/s": round(nbytes[name] / us / 1e3, 1),
+                         "flop_per_byte": round(flops[name] / nbytes[name], 1)}
+        units = skip * dims.B * dims.S + (L - skip) * M
+        points.append({"fraction": frac, "k_per_sequence": k, "rows": M, "ms_per_step": round(ms, 3),
+                       "units_per_s": round(units / (ms * 1e-3), 1), "layer_calls": per})
+        print(f"[bench] dream_sweep {frac:.0%}: {ms:.2f} ms/step", file=sys.stderr, flush=True)
+        del model
+        torch.cuda.empty_cache()
+    ref = next(p for p in points if p["fraction"] == 0.10)
+    out = {
+        "metric": METRIC, "value": ref["units_per_s"], "unit": "selected-token layer-steps/s",
+        "n_gpus": 1, "steps": steps, "warmup": 2, "ms_per_step": ref["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: X0 N(0,1), per step k tokens per sequence + N(0,0.5^2), rest + "
+                "N(0,(1e-3)^2); random-init weights N(0,0.02^2)",
+        "config": {"workload": "dream_sweep: 28 Dream-7B-shaped layers (GQA 28/4 x 128, FFN "
+                               "18944), B=16, S=2048, early skip at layer 4, alpha 0, top-k per "
+                               "sequence; value and ms_per_step at 10%", "weight_bytes_per_layer":
+                   w_bytes, "points": points},
     }
     print(json.dumps(out), flush=True)
 
