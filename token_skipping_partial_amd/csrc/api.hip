@@ -85,16 +85,19 @@ size_t dllm_workspace_bytes(int32_t op, const dllm_shape* shape, int32_t m_cap) 
         return ffn_workspace_bytes(bf16, q);
       };
       if (shape->m_plan == 0) return bytes(p);
-      // any m_plan: inside a GEMM plan class the K split only shrinks as the planned rows grow,
-      // so the first row count of each class bounds it; the attention key split is largest at
-      // one planned row (its estimate of busy workgroups is smallest there)
+      // any m_plan: the weight-streaming plans' K split only shrinks as the planned rows grow,
+      // so the first row count of each of their classes bounds it; the larger tiles' plan is the
+      // same within each 128-row interval, so one row count per interval covers them; the
+      // attention key split is largest at one planned row (its estimate of busy workgroups is
+      // smallest there)
       size_t most = bytes(p);
-      for (int r : {1, 65, 129, kWsMaxRows + 1, kG32BigRows}) {
-        if (r > m_cap) break;
+      auto cover = [&](int r) {
         p.m_plan = r;
         const size_t b = bytes(p);
         if (b > most) most = b;
-      }
+      };
+      for (int r : {1, 65, 129}) if (r <= m_cap) cover(r);
+      for (long r = kWsMaxRows + 1; r <= m_cap; r = (r + 127) / 128 * 128 + 1) cover((int)r);
       return most;
     }
     default:

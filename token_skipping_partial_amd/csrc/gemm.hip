@@ -251,10 +251,10 @@ static void launch_rmsnorm_rows(const Tin* in, const int32_t* sel_idx, const Tou
 // LDS once. Narrow N (4096) uses BN = 64 and a few K splits. At larger M, 128 x 128 tiles with
 // 2 x 2 waves.
 
-// Tiles of the 32 x 32 x 16 kernel used when more than 128 rows are selected (measured on MI355X
-// at the LLaDA-8B shapes): 256 x 256 tiles for many rows (8192), 128 x 256 for a few thousand
-// (1640), where the larger tile count balances better. Both use 32-wide K slots in a 4-slot ring
-// and 8 waves (wave tiles 64 x 128 as 4 x 2, and 64 x 64 as 2 x 4).
+// Tiles of the 32 x 32 x 16 kernel used when more than kWsMaxRows rows are selected: 256 x 256
+// and 128 x 256 (the more tiles, the better they balance over the CUs; plan_g32 chooses). Both
+// use 32-wide K slots in a 4-slot ring and 8 waves (wave tiles 64 x 128 as 4 x 2, and 64 x 64 as
+// 2 x 4).
 struct G32Shape {
   int bm, bn, bk, wm, wn, st;
 };
@@ -831,6 +831,44 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF32 g, Epi epi) {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
+// Plans of the 32 x 32 x 16 kernel (more than kWsMaxRows rows): the tile (256 x 256 or
+// 128 x 256) and K split (1, 2 or 4; the SwiGLU tiles never split) of least estimated time.
+// Workgroups run in rounds of one per CU; a round of a tile takes its flops at the tile's
+// per-CU rate plus a fixed cost, and a split adds the pass that sums the float32 partials.
+// The rates, fixed cost and reduction bandwidth were fitted to the measured times of 8 tile x
+// split plans of the four projections of the LLaDA-8B and Dream-7B layers at 320-1640 rows
+// (MI355X, kernel traces): the chosen plan is 1.3% slower than the fastest one on average, 24%
+// at worst (W_o of Dream-7B at 1640 rows), where the tile chosen before by row count alone was
+// up to 1.5x slower. Rows are rounded up to 128, so the plan is the same for every row count
+// of one 128-row interval.
+static GemmPlan plan_g32(int rows, int N, int K, bool swiglu) {
+  constexpr double kRate[2][2] = {{6.35e6, 5.42e6},   // flops per us per CU: {256, 128} rows,
+                                  {7.16e6, 5.73e6}};  // without / with SwiGLU
+  constexpr double kRoundUs = 9.4, kReduceBytesPerUs = 6.0e6, kReduceUs = 2.0;
+  const double mp = (double)((rows + 127) / 128 * 128);
+  const G32Shape cand[2] = {kG32Big, kG32Mid};
+  GemmPlan best{};
+  double best_t = 0.0;
+  for (int c = 0; c < 2; ++c) {
+    const G32Shape& t = cand[c];
+    const int cols = swiglu ? t.bn / 2 : t.bn;
+    const long tiles = (long)((N + cols - 1) / cols) * (long)((mp + t.bm - 1) / t.bm);
+    for (int s = 1; s <= (swiglu ? 1 : 4); s *= 2) {
+      if (s > 1 && (K + s - 1) / s < 512) break;
+      const long wg = tiles * s;
+      const long rounds = (wg + 255) / 256;
+      const int kc = ((K + s - 1) / s + t.bk - 1) / t.bk * t.bk;
+      double us = rounds * (2.0 * t.bm * t.bn * kc / kRate[swiglu][c] + kRoundUs);
+      if (s > 1) us += (double)s * mp * N * 4.0 / kReduceBytesPerUs + kReduceUs;
+      if (best_t == 0.0 || us < best_t) {
+        best_t = us;
+        best = GemmPlan{t.bm, t.bn, t.bk, t.wm, t.wn, t.st, s, 32};
+      }
+    }
+  }
+  return best;
+}
+
 // Weight-streaming plans (M <= 128). Every tile covers all selected rows, so each workgroup
 // re-reads the K-slice of X it needs next to its weight slab; one workgroup per CU (about 256
 // tiles) streams disjoint slabs. Measured on MI355X at the LLaDA-8B layer shape (M = 128), the
@@ -847,12 +885,13 @@ GemmPlan plan_gemm(bool bf16, int rows, int N, int K, bool swiglu) {
   GemmPlan p{64, 64, 64, 4, 1, 4, 1};
   if (!bf16) return p;
   if (rows > kWsMaxRows) {
-    const G32Shape t = rows >= kG32BigRows ? kG32Big : kG32Mid;
-    p = GemmPlan{t.bm, t.bn, t.bk, t.wm, t.wn, t.st, 1, 32};
-    const long tiles = (long)cdiv(N, swiglu ? p.bn / 2 : p.bn) * cdiv(rows, p.bm);
-    if (!swiglu)
-      while (tiles * p.splits < 256 && K / (p.splits * 2) >= 512 && p.splits < 8) p.splits *= 2;
-    return p;
+#ifdef DLLM_G32_FORCE
+    {
+      const G32Shape t = DLLM_G32_FORCE == 0 ? kG32Big : kG32Mid;
+      return GemmPlan{t.bm, t.bn, t.bk, t.wm, t.wn, t.st, DLLM_G32_SPLIT, 32};
+    }
+#endif
+    return plan_g32(rows, N, K, swiglu);
   }
   const int bm = rows <= 64 ? 64 : rows <= 128 ? 128 : 256;
   const int wm = bm / 32;  // waves of 32 rows

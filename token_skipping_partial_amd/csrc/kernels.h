@@ -43,15 +43,12 @@ struct ProjShape {
 };
 
 // GEMM plan classes by planned rows: weight-streaming tiles that hold every row up to
-// kWsMaxRows (64 / 128 / 256-row tiles), then 32 x 32 x 16 tiles, the big ones from kG32BigRows.
+// kWsMaxRows (64 / 128 / 256-row tiles), then 32 x 32 x 16 tiles (256 x 256 or 128 x 256, by an
+// estimate of their time).
 #ifndef DLLM_WS_MAX_ROWS
 #define DLLM_WS_MAX_ROWS 256
 #endif
 constexpr int kWsMaxRows = DLLM_WS_MAX_ROWS;
-#ifndef DLLM_G32_BIG_ROWS
-#define DLLM_G32_BIG_ROWS 4096
-#endif
-constexpr int kG32BigRows = DLLM_G32_BIG_ROWS;
 
 // launch plan of one GEMM: tile height, number of K splits
 struct GemmPlan {
