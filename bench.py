@@ -478,7 +478,8 @@ def run_dream_sweep(args):
         t1.record(stream)
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / steps
-        # the three calls of layer `skip` on this step's rows, one event pair each (3 repeats)
+        # the three calls of layer `skip` on this step's rows, one event pair around 20 repeats of
+        # each (enough for the host to run ahead of the GPU, so launch latency is not timed)
         s1, sc, w = model.step1, model.sparse, layers[skip]
         calls = {
             "gather_qkv_scatter_kv": lambda: tsp.dllm_gather_qkv_scatter_kv(
@@ -503,11 +504,11 @@ def run_dream_sweep(args):
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for _ in range(3):
+            for _ in range(20):
                 fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / 3 * 1e3
+            us = e0.elapsed_time(e1) / 20 * 1e3
             per[name] = {"us": round(us, 1), "TFLOP/s": round(flops[name] / us / 1e6, 1),
                          "GB/s": round(nbytes[name] / us / 1e3, 1),
                          "flop_per_byte": round(flops[name] / nbytes[name], 1)}

@@ -188,14 +188,19 @@ def test_select_batched_step_size(lib):
     check_select(lib, score, None, O.SEL_TOPK, k=1024)
 
 
-@pytest.mark.parametrize("m_plan", [1, 128, 200, 300, 5000])
+@pytest.mark.parametrize("m_plan", [1, 128, 200, 300, 700, 1640, 5000])
 def test_planned_rows_do_not_change_results(lib, m_plan):
-    """LLaDA-8B layer (B=1, S=1024), 200 selected rows, capacity every token, and plans made for
-    1 (64-row tiles, 4 row tiles), 128, 200 (256-row tiles), 300 (32x32 tiles with K splits) and
-    more than the capacity: every selected row is still computed and matches the oracle, and
-    nothing else is written. Each call takes its inputs from the generators."""
-    d = W.LLADA_LAYER
-    print(f"planned rows {m_plan}", flush=True)
+    """LLaDA-8B layer, 200 selected rows per sequence, capacity every token, and the calls planned
+    for other row counts: every selected row is still computed and matches the oracle, and nothing
+    else is written. The planned counts reach every GEMM plan class at this shape: 1 (64-row
+    weight-streaming tiles, 4 row tiles), 128, 200 (256-row tiles); then the 32x32x16 tiles
+    chosen by their estimated time: 300 (128 x 256, unsplit and 4 K splits), 700 (256 x 256
+    unsplit and with 4 splits, 128 x 256 with 2), 1640 (256 x 256 with 2 splits) and 5000
+    (256 x 256 unsplit). Up to 1024 planned rows the layer is one sequence of 1024 tokens, above
+    it 8 sequences (plans are capped at the capacity). Each call takes its inputs from the
+    generators."""
+    d = W.LLADA_LAYER if m_plan <= 1024 else W.LLADA_STEP
+    print(f"planned rows {m_plan}, B={d.B}", flush=True)
     sel, rp = even_selection(d.B, d.S, 200, 61)
     M, cap = int(rp[-1]), d.B * d.S
     w = weights_gpu(d, 930)
