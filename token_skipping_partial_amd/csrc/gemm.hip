@@ -837,9 +837,9 @@ static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 // per-CU rate plus a fixed cost, and a split adds the pass that sums the float32 partials.
 // The rates, fixed cost and reduction bandwidth were fitted to the measured times of 8 tile x
 // split plans of the four projections of the LLaDA-8B and Dream-7B layers at 320-1640 rows
-// (MI355X, kernel traces): the chosen plan is 1.3% slower than the fastest one on average, 24%
-// at worst (W_o of Dream-7B at 1640 rows), where the tile chosen before by row count alone was
-// up to 1.5x slower. Rows are rounded up to 128, so the plan is the same for every row count
+// (MI355X, kernel traces): the chosen plan is 1.5% slower than the fastest one on average, 23%
+// at worst (W_o of Dream-7B at 1632 rows), where the tile chosen before by row count alone was
+// up to 1.4x slower. Rows are rounded up to 128, so the plan is the same for every row count
 // of one 128-row interval.
 static GemmPlan plan_g32(int rows, int N, int K, bool swiglu) {
   constexpr double kRate[2][2] = {{6.35e6, 5.42e6},   // flops per us per CU: {256, 128} rows,
