@@ -51,6 +51,29 @@ __device__ __forceinline__ float variation(const HidSums& a, int kind, int d) {
 }
 
 // online (max, sum 2^(z*log2e - max)) over a strided part of a logits row, in log2 units
+// The logits are read exactly once: non-temporal loads keep them from displacing other data in
+// the caches (measured on MI355X at the LLaDA-8B layer, 1024 x 126464 bf16 logits: 57.8 -> 49.3 us,
+// 4.8 -> 5.6 TB/s).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ void load8_stream(const T* p, float v[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const f32x4v a = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+    const f32x4v b = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p) + 1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void logit_accumulate(const T* z, long V, int lane, int nlanes,
                                                  float& m, float& s) {
@@ -60,7 +83,7 @@ __device__ __forceinline__ void logit_accumulate(const T* z, long V, int lane, i
   for (; i + (kU - 1) * step + 8 <= V; i += kU * step) {
     float v[kU][8];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) Elem<T>::load8(z + i + u * step, v[u]);
+    for (int u = 0; u < kU; ++u) load8_stream<T>(z + i + u * step, v[u]);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       float cm = v[u][0];
@@ -77,7 +100,7 @@ __device__ __forceinline__ void logit_accumulate(const T* z, long V, int lane, i
   }
   for (; i + 8 <= V; i += step) {
     float v[8];
-    Elem<T>::load8(z + i, v);
+    load8_stream<T>(z + i, v);
     float cm = v[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) cm = fmaxf(cm, v[e]);
