@@ -500,6 +500,10 @@ void attn_bf16_kernel(AttnArgs a) {
   // Software pipeline over the 4-slot ring: while the exponentials of tile it are computed on the
   // vector units, the matrix cores already form the scores of tile it+1; then tile it's products
   // with V. Tile t is loaded 3 tiles ahead into the slot that tile t-4 used.
+  // A wave whose 32 query rows all lie past the last one (the tail of the last query tile) still
+  // loads its share of every tile and meets every barrier, but forms no scores or products: the
+  // matrix cores of its SIMD are left to the other wave there.
+  const bool live = tile0 + 32 * wave < nrows;
   if (!DELTA || ntile > 0) {  // (a stable-token pass over a sequence with no change has no tile)
 #pragma unroll
     for (int s = 0; s < ST - 1; ++s)
@@ -509,8 +513,10 @@ void attn_bf16_kernel(AttnArgs a) {
     else attn_wait_vm<0>();
     asm volatile("s_barrier" ::: "memory");
     f32x16 sa[2], sb[2];
-    scores(ring, sa);
-    mask_tail(sa, 0);
+    if (live) {
+      scores(ring, sa);
+      mask_tail(sa, 0);
+    }
     bf16x8 pf[4];
 
     for (int it = 0; it + 1 < ntile; ++it) {
@@ -519,16 +525,20 @@ void attn_bf16_kernel(AttnArgs a) {
       else attn_wait_vm<0>();
       asm volatile("s_barrier" ::: "memory");
       if (it + 3 < ntile) issue(it + 3, ring + ((it + 3) % ST) * SLOT);
-      reference(sa);
-      scores_expo(ring + ((it + 1) % ST) * SLOT, sb, sa, pf);
-      pv(it % ST, pf);
-      mask_tail(sb, it + 1);
+      if (live) {
+        reference(sa);
+        scores_expo(ring + ((it + 1) % ST) * SLOT, sb, sa, pf);
+        pv(it % ST, pf);
+        mask_tail(sb, it + 1);
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) sa[kb2] = sb[kb2];
+        for (int kb2 = 0; kb2 < 2; ++kb2) sa[kb2] = sb[kb2];
+      }
     }
-    reference(sa);
-    expo(sa, pf);
-    pv((ntile - 1) % ST, pf);
+    if (live) {
+      reference(sa);
+      expo(sa, pf);
+      pv((ntile - 1) % ST, pf);
+    }
   }
 
   // oacc[hb][rr] = unnormalised o[query n][hd 32 hb + 8 (rr/4) + 4 h + rr%4]
