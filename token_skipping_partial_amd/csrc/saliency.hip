@@ -20,21 +20,42 @@ struct HidSums {
 };
 
 template <typename T>
+__device__ __forceinline__ void load8_stream(const T* p, float v[8]);
+
+__device__ __forceinline__ void hid_add(HidSums& a, const float (&xv)[8], const float (&yv)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float df = xv[e] - yv[e];
+    a.s1 += fabsf(df);
+    a.s2 = fmaf(df, df, a.s2);
+    a.sx = fmaf(xv[e], xv[e], a.sx);
+    a.sy = fmaf(yv[e], yv[e], a.sy);
+    a.sd = fmaf(df, xv[e] + yv[e], a.sd);
+  }
+}
+
+// both hidden rows are read once: up to 4 pairs of 16-byte loads in flight per lane
+template <typename T>
 __device__ __forceinline__ void hid_accumulate(const T* x, const T* y, int d, int lane,
                                                int nlanes, HidSums& a) {
-  for (int i = lane * 8; i < d; i += nlanes * 8) {
-    float xv[8], yv[8];
-    Elem<T>::load8(x + i, xv);
-    Elem<T>::load8(y + i, yv);
+  constexpr int kU = 4;
+  const int step = nlanes * 8;
+  int i = lane * 8;
+  for (; i + (kU - 1) * step + 8 <= d; i += kU * step) {
+    float xv[kU][8], yv[kU][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float df = xv[e] - yv[e];
-      a.s1 += fabsf(df);
-      a.s2 = fmaf(df, df, a.s2);
-      a.sx = fmaf(xv[e], xv[e], a.sx);
-      a.sy = fmaf(yv[e], yv[e], a.sy);
-      a.sd = fmaf(df, xv[e] + yv[e], a.sd);
+    for (int u = 0; u < kU; ++u) {
+      load8_stream<T>(x + i + u * step, xv[u]);
+      load8_stream<T>(y + i + u * step, yv[u]);
     }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) hid_add(a, xv[u], yv[u]);
+  }
+  for (; i < d; i += step) {
+    float xv[8], yv[8];
+    load8_stream<T>(x + i, xv);
+    load8_stream<T>(y + i, yv);
+    hid_add(a, xv, yv);
   }
 }
 
