@@ -885,12 +885,6 @@ GemmPlan plan_gemm(bool bf16, int rows, int N, int K, bool swiglu) {
   GemmPlan p{64, 64, 64, 4, 1, 4, 1};
   if (!bf16) return p;
   if (rows > kWsMaxRows) {
-#ifdef DLLM_G32_FORCE
-    {
-      const G32Shape t = DLLM_G32_FORCE == 0 ? kG32Big : kG32Mid;
-      return GemmPlan{t.bm, t.bn, t.bk, t.wm, t.wn, t.st, DLLM_G32_SPLIT, 32};
-    }
-#endif
     return plan_g32(rows, N, K, swiglu);
   }
   const int bm = rows <= 64 ? 64 : rows <= 128 ? 128 : 256;
