@@ -188,19 +188,28 @@ def test_select_batched_step_size(lib):
     check_select(lib, score, None, O.SEL_TOPK, k=1024)
 
 
-@pytest.mark.parametrize("m_plan", [1, 128, 200, 300, 700, 1640, 5000])
-def test_planned_rows_do_not_change_results(lib, m_plan):
-    """LLaDA-8B layer, 200 selected rows per sequence, capacity every token, and the calls planned
+PLANNED = [("llada", p) for p in (1, 128, 200, 300, 700, 1640, 5000)] + \
+          [("dream", p) for p in (320, 656, 3280)]
+
+
+@pytest.mark.parametrize("shape_name,m_plan", PLANNED, ids=[f"{n}-{p}" for n, p in PLANNED])
+def test_planned_rows_do_not_change_results(lib, shape_name, m_plan):
+    """A layer with 200 selected rows per sequence, capacity every token, and the calls planned
     for other row counts: every selected row is still computed and matches the oracle, and nothing
-    else is written. The planned counts reach every GEMM plan class at this shape: 1 (64-row
-    weight-streaming tiles, 4 row tiles), 128, 200 (256-row tiles); then the 32x32x16 tiles
-    chosen by their estimated time: 300 (128 x 256, unsplit and 4 K splits), 700 (256 x 256
+    else is written. LLaDA-8B: the planned counts reach every GEMM plan class at this shape: 1
+    (64-row weight-streaming tiles, 4 row tiles), 128, 200 (256-row tiles); then the 32x32x16
+    tiles chosen by their estimated time: 300 (128 x 256, unsplit and 4 K splits), 700 (256 x 256
     unsplit and with 4 splits, 128 x 256 with 2), 1640 (256 x 256 with 2 splits) and 5000
-    (256 x 256 unsplit). Up to 1024 planned rows the layer is one sequence of 1024 tokens, above
-    it 8 sequences (plans are capped at the capacity). Each call takes its inputs from the
-    generators."""
-    d = W.LLADA_LAYER if m_plan <= 1024 else W.LLADA_STEP
-    print(f"planned rows {m_plan}, B={d.B}", flush=True)
+    (256 x 256 unsplit); up to 1024 planned rows the layer is one sequence of 1024 tokens, above it
+    8 sequences (plans are capped at the capacity). Dream-7B (GQA 28/4, d 3584, FFN 18944, 16 x
+    2048 tokens): 320 (128 x 256 with 4 splits over K = 3584), 656 (128 x 256 with 2 splits;
+    256 x 256 with 4 splits over K = 18944) and 3280 (256 x 256). Each call takes its inputs from
+    the generators."""
+    if shape_name == "llada":
+        d = W.LLADA_LAYER if m_plan <= 1024 else W.LLADA_STEP
+    else:
+        d = W.DREAM_GQA
+    print(f"planned rows {m_plan}, {shape_name} B={d.B}", flush=True)
     sel, rp = even_selection(d.B, d.S, 200, 61)
     M, cap = int(rp[-1]), d.B * d.S
     w = weights_gpu(d, 930)
