@@ -1,18 +1,20 @@
 """Benchmark of the token-skipping denoising step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload llada_layer]
+    python bench.py [--gpus 1] [--steps 16] [--warmup 3] [--workload llada_step]
 
-Default workload: one LLaDA-8B-shaped layer (bf16, B=1, S=1024, d=4096, 32 heads x 128,
-FFN 12288, vocabulary 126464). A step is the whole hot path on one batch:
-saliency (alpha = 0.5, L1-normalised delta + max-softmax confidence) -> top-128 selection ->
-gathered QKV + K/V scatter -> partial attention -> gathered FFN + hidden scatter.
-16 independent sets of weights/logits/hidden/caches rotate from step to step so that no set is
-still resident in the 256 MB last-level cache; every input is in HBM before the timed region.
+Default workload (llada_step): one full denoising step of 32 LLaDA-8B-shaped layers (bf16, B=8,
+S=1024, d=4096, 32 heads x 128, FFN 12288, vocabulary 126464) with early skip at layer 4: layers
+0-3 on every token, saliency of the layer-4 input against the previous step (alpha = 0.5,
+L1-normalised delta + max-softmax confidence of fresh previous-step logits), top-205 selection per
+sequence, layers 4-31 on the 1640 selected rows against the cached K/V; the layer-0 input moves
+from step to step and every cache is carried across steps. Inputs are resident in HBM before the
+timed region.
 
-Metric: selected-token layer-steps per second (selected rows x selected layers per second).
-Rank 0 prints one JSON line with the step rate, the roofline of the dominant kernel (HIP events
-around its launch inside the timed region), the partial-attention HBM rate, and the CPU oracle
-timed on a bounded sample of the same workload.
+Metric: selected-token layer-steps per second (rows x layers run per second: 4 x 8192 + 28 x
+1640 per step). Rank 0 prints one JSON line with the step rate, the roofline of the call that
+takes the most time per step (HIP events at every call boundary inside the timed region), the
+partial-attention HBM rate inside the step, and the CPU oracle timed on sampled rows of the
+same workload. `--workload llada_layer` runs the single-layer configuration (B=1, top-128).
 """
 from __future__ import annotations
 
@@ -37,13 +39,13 @@ METRIC = "selected-token layer-steps/sec at 8B shape; partial-attn HBM GB/s % pe
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="llada_layer",
+    p.add_argument("--steps", type=int, default=16)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="llada_step",
                    choices=["llada_layer", "llada_step", "llada_context", "llada_adaptive",
                             "llada_response", "llada_decode", "dream_sweep"],
-                   help="llada_layer: one LLaDA-8B-shaped layer, B=1 (default); llada_step: the "
-                        "full 32-layer early-skip step, B=8, S=1024, top-205 per sequence; "
+                   help="llada_step (default): the full 32-layer early-skip step, B=8, S=1024, "
+                        "top-205 per sequence; llada_layer: one LLaDA-8B-shaped layer, B=1; "
                         "llada_context: the llada_layer step keeping the attention context of "
                         "every token (exact rows for the selected, changed-key update for the rest); "
                         "llada_adaptive: 32 LLaDA-8B layers, B=1, S=1024, per-layer FFN rows chosen "
@@ -133,7 +135,12 @@ def main():
     if args.workload in ("llada_adaptive", "llada_response"):
         run_llada_adaptive(args, response=args.workload == "llada_response")
         return
+    run_llada_layer(args)
 
+
+def run_llada_layer(args):
+    """One LLaDA-8B-shaped layer step, B=1, S=1024, top-128 of 1024 tokens, 16 rotated sets of
+    weights, logits, hidden states and caches (so no set is still in the last-level cache)."""
     import token_skipping_partial_amd as tsp  # raises if libdllm.so is not built
     from synth import workloads as W
     from token_skipping_partial_amd.step import (LayerScratch, LayerWeights, SelectConfig,
@@ -285,10 +292,54 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+class CallMarks:
+    """HIP events recorded at every call boundary of a step (on the stream the calls run on).
+    After a synchronisation, durations() gives, per call name, the sum and count of the
+    intervals that end at that name's events."""
+
+    def __init__(self, stream, capacity: int):
+        self.stream = stream
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        self.tags = []
+
+    def start(self):
+        self.tags = ["start"]
+        self.events[0].record(self.stream)
+
+    def __call__(self, tag):
+        self.events[len(self.tags)].record(self.stream)
+        self.tags.append(tag)
+
+    def durations(self, into: dict):
+        for i in range(1, len(self.tags)):
+            ms = self.events[i - 1].elapsed_time(self.events[i])
+            tot, n = into.get(self.tags[i], (0.0, 0))
+            into[self.tags[i]] = (tot + ms, n + 1)
+
+
+def call_work(dims, rows: int):
+    """Algorithmic flops and HBM bytes of one launch of each layer call on `rows` selected rows
+    (what the method must compute and move: weights once, each selected row's activations, the
+    K/V cache read once per (sequence, kv head)), bf16 storage."""
+    b = 2
+    nq, nkv = dims.H * dims.hd, dims.Hkv * dims.hd
+    nqkv = nq + 2 * nkv
+    return {
+        "qkv": {"flops": 2.0 * rows * nqkv * dims.d,
+                "bytes": b * (nqkv * dims.d + dims.d + rows * (dims.d + nqkv)) + 4 * rows},
+        "attn": {"flops": 4.0 * rows * dims.S * nq,
+                 "bytes": b * (2 * rows * nq + 2 * dims.B * dims.S * nkv) + 4 * (rows + dims.B + 1)},
+        "ffn": {"flops": 2.0 * rows * (dims.d * nq + 3 * dims.F * dims.d),
+                "bytes": b * (dims.d * nq + 3 * dims.F * dims.d + 2 * dims.d
+                              + rows * (nq + 2 * dims.d)) + 4 * rows},
+    }
+
+
 def run_llada_step(args):
     """32 LLaDA-8B layers, B=8, S=1024: layers 0-3 on every token, saliency at layer 4 (alpha 0.5,
     fresh previous-step logits), top-205 per sequence, layers 4-31 on the selected rows against the
-    cached K/V. Hidden input X^t = X^(t-1) + per-step perturbation; caches carried across steps."""
+    cached K/V. Hidden input X^t = X^(t-1) + per-step perturbation; caches carried across steps.
+    The timed region holds the steps back to back with an event at every call boundary."""
     import synth
     import token_skipping_partial_amd as tsp
     from synth import workloads as W
@@ -311,16 +362,21 @@ def run_llada_step(args):
         large = synth.large_positions(dims.B, dims.S, W.LLADA_LARGE, seed=7600 + t, device="cuda")
         xs.append(synth.perturb(xs[-1], large, seed=7700 + t))
     logits = [synth.logits(dims.B, dims.S, dims.V, seed=7800 + i, device="cuda") for i in range(4)]
+    print("[bench] inputs resident; fill step", file=sys.stderr, flush=True)
     model.fill(xs[0])
     for t in range(args.warmup):
         model.step(xs[1 + t], logits[t % 4])
     torch.cuda.synchronize()
+    print("[bench] warm; timing", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
+    marks = [CallMarks(stream, 8 * L + 16) for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0.record(stream)
     for t in range(args.steps):
         i = args.warmup + t
-        model.step(xs[1 + i], logits[i % 4])
+        marks[t].start()
+        model.step(xs[1 + i], logits[i % 4], mark=marks[t])
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
@@ -328,6 +384,49 @@ def run_llada_step(args):
     skip2 = args.second_skip or L
     M2 = int(model.step2.row_ptr[-1].item()) if args.second_skip else M
     units = skip * dims.B * dims.S + (skip2 - skip) * M + (L - skip2) * M2
+
+    # per call class: total per step, launches per step, mean per launch, algorithmic rates
+    acc = {}
+    for mk in marks:
+        mk.durations(acc)
+    rows_of = {"dense": dims.B * dims.S, "sel": M, "sel2": M2}
+    calls = {}
+    for tag, (tot, n) in acc.items():
+        entry = {"ms_per_step": round(tot / args.steps, 4), "launches_per_step": n // args.steps,
+                 "us_per_launch": round(tot / n * 1e3, 2)}
+        kind, _, call = tag.partition("_")
+        if call in ("qkv", "attn", "ffn"):
+            w = call_work(dims, rows_of[kind])[call]
+            us = tot / n * 1e3
+            entry.update({"rows": rows_of[kind], "flops_per_launch": w["flops"],
+                          "bytes_per_launch": w["bytes"],
+                          "TFLOP/s": round(w["flops"] / us / 1e6, 1),
+                          "GB/s": round(w["bytes"] / us / 1e3, 1)})
+        calls[tag] = entry
+    # roofline: the layer call that takes the most time per step
+    dom = max((t for t in calls if "flops_per_launch" in calls[t]),
+              key=lambda t: calls[t]["ms_per_step"])
+    d = calls[dom]
+    ai = d["flops_per_launch"] / d["bytes_per_launch"]
+    ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai >= ridge:
+        roof = {"bound": "mfma", "achieved": d["TFLOP/s"], "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(d["TFLOP/s"] / MFMA_BF16_PEAK_TFS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": d["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(d["GB/s"] / HBM_PEAK_GBS, 4)}
+    roofline = {"kernel": f"{dom}: {CALL_KERNELS[dom.partition('_')[2]]}",
+                **roof, "traffic": call_traffic(dom)}
+    pa = calls.get("sel_attn")
+    partial_attn = None
+    if pa:
+        partial_attn = {"achieved": pa["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(pa["GB/s"] / HBM_PEAK_GBS, 4), "rows": M,
+                        "us_per_launch": pa["us_per_launch"],
+                        "kernel": CALL_KERNELS["attn"]}
+    cpu = None
+    if args.cpu_seconds > 0 and not args.second_skip:
+        cpu = cpu_baseline_step(dims, L, skip, M, args.cpu_seconds)
     out = {
         "metric": METRIC, "value": round(units / (ms * 1e-3), 1),
         "unit": "selected-token layer-steps/s", "n_gpus": 1, "steps": args.steps,
@@ -335,15 +434,106 @@ def run_llada_step(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: X0 N(0,1), per step 154 tokens per sequence + N(0,0.5^2), rest + "
                 "N(0,(1e-3)^2); logits N(0,3^2); random-init weights N(0,0.02^2)",
-        "config": {"workload": "llada_step: 32 LLaDA-8B-shaped layers, B=8, S=1024, early skip at "
-                               "layer 4, alpha=0.5, top-205 per sequence",
+        "config": {"workload": "llada_step: 32 LLaDA-8B-shaped layers, B=8, S=1024, d=4096, 32x128 "
+                               "MHA, FFN 12288, V=126464, early skip at layer 4, alpha=0.5, "
+                               "top-205 per sequence",
                    "units_per_step": units, "selected_per_step": M},
+        "roofline": roofline,
+        "partial_attn": partial_attn,
+        "calls": calls,
+        "cpu_baseline": cpu,
     }
     if args.second_skip:
         out["config"]["workload"] += (f", second skip point at layer {args.second_skip} keeping "
                                       f"top-{k2} of those per sequence")
         out["config"]["selected_after_second_skip"] = M2
     print(json.dumps(out), flush=True)
+
+
+# kernels each layer call launches (bf16, the planned shapes of the llada_step workload)
+CALL_KERNELS = {
+    "qkv": "dllm_gather_qkv_scatter_kv (gather + RMSNorm, then the QKV GEMM whose epilogue writes "
+           "q rows and scatters K/V rows into the cache)",
+    "attn": "dllm_partial_attn (attention over every cached key; split-key merge when planned)",
+    "ffn": "dllm_gather_ffn_scatter (W_o GEMM + residual, RMSNorm, gate/up GEMM with SwiGLU, "
+           "W_down GEMM + residual + scatter)",
+}
+
+
+def call_traffic(tag: str):
+    """Measured HBM bytes per launch of a call class from profiles/traffic.json (FETCH_SIZE and
+    WRITE_SIZE of the call's kernels, scaled by the copy calibration), or None when a source
+    file has changed since the counters were taken or none were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get("llada_step/" + tag)
+    if not rec:
+        return None
+    for src, digest in rec.get("sources", {}).items():
+        with open(os.path.join(ROOT, src), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline_step(dims, L: int, skip: int, M: int, budget_s: float):
+    """The CPU oracle on the llada_step workload, extrapolated from sampled rows: saliency of a
+    sample of tokens (full vocabulary), the selection of every sequence, and the three layer
+    calls on 64 rows; rows are independent given their inputs, so the step's time is the
+    sample's scaled to 4 x 8192 + 28 x M layer rows and 8192 scored tokens. The sample runs on
+    synthetic inputs of the same shapes drawn on the host."""
+    import numpy as np
+
+    import oracle as O
+    import synth
+
+    rng_rows = 64
+    scale = 1.0 / math.sqrt(dims.hd)
+    w = {k: O.decode_bf16(v.view(torch.uint16).numpy()) for k, v in
+         synth.layer_weights(dims.d, dims.H, dims.Hkv, dims.hd, dims.F, seed=5000).items()}
+    h = O.decode_bf16(synth.normal((1, dims.S, dims.d), 1.0, 5001, torch.bfloat16)
+                      .view(torch.uint16).numpy())
+    kc = O.decode_bf16(synth.normal((1, dims.Hkv, dims.S, dims.hd), 1.0, 5002, torch.bfloat16)
+                       .view(torch.uint16).numpy())
+    vc = O.decode_bf16(synth.normal((1, dims.Hkv, dims.S, dims.hd), 1.0, 5003, torch.bfloat16)
+                       .view(torch.uint16).numpy())
+    sel = np.arange(0, dims.S, dims.S // rng_rows, dtype=np.int32)[:rng_rows]
+    rp = np.array([0, sel.size], dtype=np.int32)
+    t0 = time.perf_counter()
+    n_layer = 0
+    while True:
+        O.selected_layer(h, w, sel, rp, kc, vc, h, dims.H, dims.Hkv, dims.hd, 1e-5, scale)
+        n_layer += 1
+        if time.perf_counter() - t0 >= budget_s * 0.6:
+            break
+    t_layer = (time.perf_counter() - t0) / n_layer
+    n_tok = 64
+    hc = O.decode_bf16(synth.normal((n_tok, dims.d), 1.0, 5004, torch.bfloat16).view(torch.uint16).numpy())
+    hp = O.decode_bf16(synth.normal((n_tok, dims.d), 1.0, 5005, torch.bfloat16).view(torch.uint16).numpy())
+    lg = O.decode_bf16(synth.logits(1, n_tok, dims.V, seed=5006).view(torch.uint16).numpy())[0]
+    t0 = time.perf_counter()
+    O.saliency(hc, hp, lg, 0.5)
+    t_sal = time.perf_counter() - t0
+    score = np.random.default_rng(5007).standard_normal((dims.B, dims.S)).astype(np.float32)
+    t0 = time.perf_counter()
+    O.select_compact(score, None, O.SEL_TOPK, k=M // dims.B)
+    t_sel = time.perf_counter() - t0
+    layer_rows = skip * dims.B * dims.S + (L - skip) * M
+    t_step = (layer_rows / rng_rows * t_layer + dims.B * dims.S / n_tok * t_sal + t_sel)
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max(i.get("num_threads", 1) for i in threadpool_info())
+    except Exception:
+        blas_threads = os.cpu_count()
+    return {"value": round(layer_rows / t_step, 2), "unit": "selected-token layer-steps/s",
+            "cores": blas_threads, "kind": "oracle",
+            "sample": f"extrapolated: {n_layer} oracle layer calls (QKV, attention, FFN) on "
+                      f"{rng_rows} rows ({t_layer:.2f} s each), saliency of {n_tok} tokens over "
+                      f"the full vocabulary, selection of {dims.B} sequences; scaled to "
+                      f"{layer_rows} layer rows and {dims.B * dims.S} scored tokens per step "
+                      f"(float64 numpy, BLAS on {blas_threads} threads, the rest on one)"}
 
 
 def run_llada_decode(args):

@@ -45,9 +45,13 @@
  *     global state; calls are re-entrant.
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously; no
  *     call synchronises the device.
- *   - All arguments are validated on the host before anything is enqueued. A return value other
- *     than DLLM_OK means nothing was enqueued and nothing was written. Execution faults surface at
- *     the caller's next synchronisation.
+ *   - All arguments are validated on the host before anything is enqueued. DLLM_ERR_INVALID_ARG,
+ *     DLLM_ERR_UNSUPPORTED and DLLM_ERR_WORKSPACE mean nothing was enqueued and nothing was
+ *     written. DLLM_ERR_HIP means the runtime rejected a kernel launch; a call that makes several
+ *     launches (projection, attention and FFN calls, dllm_salient_attn, dllm_commit) may then
+ *     have enqueued the launches before the rejected one, so its outputs and any state it
+ *     updates in place (caches, softmax state) are undefined until the call succeeds again.
+ *     Execution faults surface at the caller's next synchronisation.
  *   - One storage type per call (shape->dtype) covers every tensor except: scores, confidences and
  *     deltas are float32; indices are int32; the force mask is uint8.
  *   - bf16 tensors are multiplied on the matrix cores with float32 accumulation; norms, softmax

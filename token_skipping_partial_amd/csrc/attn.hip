@@ -729,9 +729,6 @@ static AttnCfg plan_bf16(const ProjShape& s) {
   const int G = s.H / s.Hkv;
   const long rows_avg = (long)cdiv((long)s.m_plan * G, s.B);
   c.nw = (s.hd == 128 || rows_avg > 160) ? 8 : 4;
-#ifdef DLLM_ATTN_FORCE_NW
-  c.nw = DLLM_ATTN_FORCE_NW;
-#endif
   c.st = 4;
   const long slots = 256L * ((c.nw == 8 && s.hd == 128) ? 1 : 2);
   const long est = (long)s.B * s.Hkv * (rows_avg > 0 ? cdiv(rows_avg, 32 * c.nw) : 1);

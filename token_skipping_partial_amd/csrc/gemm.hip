@@ -258,14 +258,8 @@ static void launch_rmsnorm_rows(const Tin* in, const int32_t* sel_idx, const Tou
 struct G32Shape {
   int bm, bn, bk, wm, wn, st;
 };
-#ifndef DLLM_G32_BIG   // tile override for timing builds: bm, bn, bk, wm, wn, ring slots
-#define DLLM_G32_BIG 256, 256, 32, 4, 2, 4
-#endif
-#ifndef DLLM_G32_MID
-#define DLLM_G32_MID 128, 256, 32, 2, 4, 4
-#endif
-constexpr G32Shape kG32Big{DLLM_G32_BIG};
-constexpr G32Shape kG32Mid{DLLM_G32_MID};
+constexpr G32Shape kG32Big{256, 256, 32, 4, 2, 4};  // bm, bn, bk, wm, wn, ring slots
+constexpr G32Shape kG32Mid{128, 256, 32, 2, 4, 4};
 
 // ring slots that fit in the 160 KB of LDS a workgroup may use, capped at `want`
 constexpr int ring_slots(int bm, int bn, int bk, int want) {
@@ -386,7 +380,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g, Epi
   // All workgroups walk K in the same order: tiles that share an X slice then read it at about
   // the same time, so it is fetched into each L2 once instead of being evicted by the weight
   // stream between readers.
-  const int rot = 0;
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -402,14 +395,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g, Epi
   for (int s = 0; s < ST - 1; ++s)
     if (s < nk)
       issue_stage<BM, BN, BK, NW, SWIGLU>(g, ring + s * SLOT, m0, n0, M,
-                                          kb + ((s + rot) % nk) * BK, wave, lane);
+                                          kb + s * BK, wave, lane);
 
   for (int kt = 0; kt < nk; ++kt) {
     wait_batches<NMIN, ST - 2>(nk - 1 - kt);  // slots issued after slot kt: min(ST-2, nk-1-kt)
     wg_barrier();
     if (kt + ST - 1 < nk)
       issue_stage<BM, BN, BK, NW, SWIGLU>(g, ring + ((kt + ST - 1) % ST) * SLOT, m0, n0, M,
-                                          kb + ((kt + ST - 1 + rot) % nk) * BK, wave, lane);
+                                          kb + (kt + ST - 1) * BK, wave, lane);
     const char* slot = ring + (kt % ST) * SLOT;
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {

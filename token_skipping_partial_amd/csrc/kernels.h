@@ -45,10 +45,7 @@ struct ProjShape {
 // GEMM plan classes by planned rows: weight-streaming tiles that hold every row up to
 // kWsMaxRows (64 / 128 / 256-row tiles), then 32 x 32 x 16 tiles (256 x 256 or 128 x 256, by an
 // estimate of their time).
-#ifndef DLLM_WS_MAX_ROWS
-#define DLLM_WS_MAX_ROWS 256
-#endif
-constexpr int kWsMaxRows = DLLM_WS_MAX_ROWS;
+constexpr int kWsMaxRows = 256;
 
 // launch plan of one GEMM: tile height, number of K splits
 struct GemmPlan {

@@ -67,16 +67,25 @@ def attn_scale(shape: Shape) -> float:
     return 1.0 / math.sqrt(shape.hd)
 
 
+def _no_mark(tag):
+    pass
+
+
 def selected_layer(shape: Shape, w: LayerWeights, h_in, k_cache, v_cache, h_out, sel_idx, row_ptr,
-                   scratch: LayerScratch, stream=None):
-    """qkv + K/V scatter, partial attention, FFN + hidden scatter for the selected rows."""
+                   scratch: LayerScratch, stream=None, mark=_no_mark, tag=""):
+    """qkv + K/V scatter, partial attention, FFN + hidden scatter for the selected rows.
+    mark(name) is called after each call is enqueued (name = tag + "qkv" / "attn" / "ffn"), so a
+    caller can record a timing event at every call boundary."""
     m = scratch.m_cap
     dllm_gather_qkv_scatter_kv(shape, h_in, w.g_attn, w.w_qkv, sel_idx, row_ptr, m,
                                scratch.q_sel, k_cache, v_cache, scratch.ws_qkv, stream)
+    mark(tag + "qkv")
     dllm_partial_attn(shape, attn_scale(shape), scratch.q_sel, k_cache, v_cache, sel_idx, row_ptr,
                       m, scratch.o_sel, scratch.ws_attn, stream)
+    mark(tag + "attn")
     dllm_gather_ffn_scatter(shape, h_in, scratch.o_sel, w.w_o, w.g_ffn, w.w_gate, w.w_up,
                             w.w_down, sel_idx, row_ptr, m, h_out, scratch.ws_ffn, stream)
+    mark(tag + "ffn")
 
 
 def all_rows(shape: Shape, device="cuda"):
@@ -110,14 +119,17 @@ class SingleLayerStep:
         self.row_ptr = torch.empty(B + 1, dtype=torch.int32, device=device)
         self.scratch = LayerScratch(shape, m_cap, device)
 
-    def score_and_select(self, h_cur, h_prev, logits, force=None, stream=None, conf=None):
+    def score_and_select(self, h_cur, h_prev, logits, force=None, stream=None, conf=None,
+                         mark=_no_mark):
         """conf: [B, S] float32; with logits the confidence is also written there, without
         logits (alpha != 0) it is read from there."""
         c = self.sel
         dllm_saliency(self.shape, c.delta_kind, c.alpha, h_cur, h_prev, logits, self.score,
                       conf, stream=stream)
+        mark("saliency")
         dllm_select_compact(self.shape, c.mode, c.tau, c.k, self.score, force, self.sel_idx,
                             self.row_ptr, stream=stream)
+        mark("select")
 
     def __call__(self, w: LayerWeights, h_cur, h_prev, logits, k_cache, v_cache, h_out,
                  force=None, stream=None):
@@ -177,32 +189,41 @@ class EarlySkipModel:
         if self.skip2:
             self.h_ref2.copy_(self.hidden[self.skip2])
 
-    def step(self, x, logits=None, force=None, stream=None):
+    def step(self, x, logits=None, force=None, stream=None, mark=_no_mark):
         """Returns the rows of the last layers: the first selection's, or with a second skip point
-        the second one's (the first is in step1.sel_idx / step1.row_ptr)."""
+        the second one's (the first is in step1.sel_idx / step1.row_ptr).
+        mark(name) is called after every call is enqueued ("copy", "dense_qkv", "dense_attn",
+        "dense_ffn", "saliency", "select", "sel_qkv", "sel_attn", "sel_ffn")."""
         self.hidden[0].copy_(x)
+        mark("copy")
         for l in range(self.skip):
             selected_layer(self.shape, self.layers[l], self.hidden[l], self.k[l], self.v[l],
-                           self.hidden[l + 1], self.all_sel, self.all_rp, self.dense, stream)
+                           self.hidden[l + 1], self.all_sel, self.all_rp, self.dense, stream,
+                           mark, "dense_")
         s = self.step1
         s.score_and_select(self.hidden[self.skip], self.h_ref, logits, force, stream,
-                           conf=self.conf if (self.skip2 and logits is not None) else None)
+                           conf=self.conf if (self.skip2 and logits is not None) else None,
+                           mark=mark)
         self.h_ref.copy_(self.hidden[self.skip])
+        mark("copy")
         last = self.skip2 or len(self.layers)
         for l in range(self.skip, last):
             selected_layer(self.shape, self.layers[l], self.hidden[l], self.k[l], self.v[l],
-                           self.hidden[l + 1], s.sel_idx, s.row_ptr, self.sparse, stream)
+                           self.hidden[l + 1], s.sel_idx, s.row_ptr, self.sparse, stream,
+                           mark, "sel_")
         if not self.skip2:
             return s.sel_idx, s.row_ptr
         s2 = self.step2
         dllm_flags_from_rows(self.shape, force, s.sel_idx, s.row_ptr, self.m_cap, self.flags2,
                              stream)
         s2.score_and_select(self.hidden[self.skip2], self.h_ref2, None, self.flags2, stream,
-                            conf=self.conf if self.sel.alpha != 0.0 else None)
+                            conf=self.conf if self.sel.alpha != 0.0 else None, mark=mark)
         self.h_ref2.copy_(self.hidden[self.skip2])
+        mark("copy")
         for l in range(self.skip2, len(self.layers)):
             selected_layer(self.shape2, self.layers[l], self.hidden[l], self.k[l], self.v[l],
-                           self.hidden[l + 1], s2.sel_idx, s2.row_ptr, s2.scratch, stream)
+                           self.hidden[l + 1], s2.sel_idx, s2.row_ptr, s2.scratch, stream,
+                           mark, "sel2_")
         return s2.sel_idx, s2.row_ptr
 
 
