@@ -37,18 +37,24 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <thread>
 #include <vector>
 
 namespace {
 
-int g_threads = 0;  // 0: one worker per hardware thread
+int g_threads = 0;  // 0: OMP_NUM_THREADS when set (the host's CPU share), else every hardware thread
 
 int workers() {
   if (g_threads > 0) return g_threads;
-  const unsigned h = std::thread::hardware_concurrency();
-  return h ? (int)h : 1;
+  const unsigned hw = std::thread::hardware_concurrency();
+  const int h = hw ? (int)hw : 1;
+  if (const char* env = std::getenv("OMP_NUM_THREADS")) {
+    const int n = std::atoi(env);
+    if (n > 0) return std::min(n, h);
+  }
+  return h;
 }
 
 // f(i) for every i in [0, n), the range cut into one contiguous block per worker
@@ -478,9 +484,11 @@ void ora_confidence_argmax(int64_t V, const void* z, int z_dt, double* conf, int
 // to S), the masked positions (tok < 0) commit the n best by (conf descending, position
 // ascending), n = max(#{conf > tau}, min(k_min, #masked)), conf compared as float32; a block
 // with no masked position left advances blk. flags = 1 over the (new) active block.
-void ora_commit(int B, int S, int64_t V, const void* logits, int lg_dt, int P, int L, float tau,
-                int k_min, int32_t* tok, int32_t* blk, int32_t* cidx, int32_t* crp,
-                uint8_t* flags) {
+// row_of (optional): position b S + s -> row of `logits` holding its logits (NULL: that same
+// index), so a caller may pass only the rows of the active blocks.
+void ora_commit(int B, int S, int64_t V, const void* logits, int lg_dt, const int32_t* row_of,
+                int P, int L, float tau, int k_min, int32_t* tok, int32_t* blk, int32_t* cidx,
+                int32_t* crp, uint8_t* flags) {
   const In Z{logits, lg_dt};
   const int nblk = (S - P + L - 1) / L;
   int32_t n_out = 0;
@@ -494,8 +502,10 @@ void ora_commit(int B, int S, int64_t V, const void* logits, int lg_dt, int P, i
         if (tok[(int64_t)b * S + s] < 0) masked.push_back(s);
       std::vector<float> conf(masked.size());
       std::vector<int64_t> arg(masked.size());
-      for (size_t i = 0; i < masked.size(); ++i)
-        conf[i] = (float)confidence_row(Z, ((int64_t)b * S + masked[i]) * V, V, &arg[i]);
+      for (size_t i = 0; i < masked.size(); ++i) {
+        const int64_t p = (int64_t)b * S + masked[i];
+        conf[i] = (float)confidence_row(Z, (row_of ? row_of[p] : p) * V, V, &arg[i]);
+      }
       int above = 0;
       for (float c : conf) above += c > tau;
       const int n = std::max(above, std::min(k_min, (int)masked.size()));
@@ -524,7 +534,7 @@ void ora_commit(int B, int S, int64_t V, const void* logits, int lg_dt, int P, i
 }
 
 // x[b, s] = emb[tok[b, s]] for a committed token, mask_emb for a masked one, at listed positions
-void ora_embed_rows(int B, int S, int d, const void* emb, int emb_dt, const void* mask_emb,
+void ora_embed_rows(int B, int /*S*/, int d, const void* emb, int emb_dt, const void* mask_emb,
                     int mask_dt, const int32_t* tok, const int32_t* sel, const int32_t* rp,
                     double* x) {
   const In E{emb, emb_dt}, Mk{mask_emb, mask_dt};
