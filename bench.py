@@ -479,40 +479,39 @@ def call_traffic(tag: str):
 
 
 def cpu_baseline_step(dims, L: int, skip: int, M: int, budget_s: float):
-    """The CPU oracle on the llada_step workload, extrapolated from sampled rows: saliency of a
-    sample of tokens (full vocabulary), the selection of every sequence, and the three layer
-    calls on 64 rows; rows are independent given their inputs, so the step's time is the
-    sample's scaled to 4 x 8192 + 28 x M layer rows and 8192 scored tokens. The sample runs on
-    synthetic inputs of the same shapes drawn on the host."""
+    """The C++ CPU oracle on the llada_step workload, extrapolated from sampled rows: the three
+    layer calls (QKV + K/V scatter, attention over every key, FFN + scatter) on 64 rows,
+    saliency of one sequence's 1024 tokens over the full vocabulary, and the selection of every
+    sequence. Rows are independent given their inputs, so the step's time is the sample's scaled
+    to 4 x 8192 + 28 x M layer rows and 8 x 1024 scored tokens. The sample runs on synthetic
+    inputs of the same shapes drawn on the host; bf16 tensors go to the oracle as bit patterns."""
     import numpy as np
 
     import oracle as O
     import synth
 
-    rng_rows = 64
+    bits = lambda t: t.contiguous().view(torch.uint16).numpy()  # noqa: E731
+    rows = 64
     scale = 1.0 / math.sqrt(dims.hd)
-    w = {k: O.decode_bf16(v.view(torch.uint16).numpy()) for k, v in
-         synth.layer_weights(dims.d, dims.H, dims.Hkv, dims.hd, dims.F, seed=5000).items()}
-    h = O.decode_bf16(synth.normal((1, dims.S, dims.d), 1.0, 5001, torch.bfloat16)
-                      .view(torch.uint16).numpy())
-    kc = O.decode_bf16(synth.normal((1, dims.Hkv, dims.S, dims.hd), 1.0, 5002, torch.bfloat16)
-                       .view(torch.uint16).numpy())
-    vc = O.decode_bf16(synth.normal((1, dims.Hkv, dims.S, dims.hd), 1.0, 5003, torch.bfloat16)
-                       .view(torch.uint16).numpy())
-    sel = np.arange(0, dims.S, dims.S // rng_rows, dtype=np.int32)[:rng_rows]
+    w = {k: bits(v) for k, v in synth.layer_weights(dims.d, dims.H, dims.Hkv, dims.hd, dims.F,
+                                                    seed=5000).items()}
+    h = bits(synth.normal((1, dims.S, dims.d), 1.0, 5001, torch.bfloat16))
+    kc = bits(synth.normal((1, dims.Hkv, dims.S, dims.hd), 1.0, 5002, torch.bfloat16))
+    vc = bits(synth.normal((1, dims.Hkv, dims.S, dims.hd), 1.0, 5003, torch.bfloat16))
+    sel = np.arange(0, dims.S, dims.S // rows, dtype=np.int32)[:rows]
     rp = np.array([0, sel.size], dtype=np.int32)
     t0 = time.perf_counter()
     n_layer = 0
     while True:
-        O.selected_layer(h, w, sel, rp, kc, vc, h, dims.H, dims.Hkv, dims.hd, 1e-5, scale)
+        O.selected_layer(h, w, sel, rp, kc, vc, h, dims.H, dims.Hkv, dims.hd, 1e-5, scale,
+                         store="bf16")
         n_layer += 1
         if time.perf_counter() - t0 >= budget_s * 0.6:
             break
     t_layer = (time.perf_counter() - t0) / n_layer
-    n_tok = 64
-    hc = O.decode_bf16(synth.normal((n_tok, dims.d), 1.0, 5004, torch.bfloat16).view(torch.uint16).numpy())
-    hp = O.decode_bf16(synth.normal((n_tok, dims.d), 1.0, 5005, torch.bfloat16).view(torch.uint16).numpy())
-    lg = O.decode_bf16(synth.logits(1, n_tok, dims.V, seed=5006).view(torch.uint16).numpy())[0]
+    hc = bits(synth.normal((dims.S, dims.d), 1.0, 5004, torch.bfloat16))
+    hp = bits(synth.normal((dims.S, dims.d), 1.0, 5005, torch.bfloat16))
+    lg = bits(synth.logits(1, dims.S, dims.V, seed=5006))[0]
     t0 = time.perf_counter()
     O.saliency(hc, hp, lg, 0.5)
     t_sal = time.perf_counter() - t0
@@ -521,19 +520,15 @@ def cpu_baseline_step(dims, L: int, skip: int, M: int, budget_s: float):
     O.select_compact(score, None, O.SEL_TOPK, k=M // dims.B)
     t_sel = time.perf_counter() - t0
     layer_rows = skip * dims.B * dims.S + (L - skip) * M
-    t_step = (layer_rows / rng_rows * t_layer + dims.B * dims.S / n_tok * t_sal + t_sel)
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max(i.get("num_threads", 1) for i in threadpool_info())
-    except Exception:
-        blas_threads = os.cpu_count()
+    t_step = layer_rows / rows * t_layer + dims.B * t_sal + t_sel
     return {"value": round(layer_rows / t_step, 2), "unit": "selected-token layer-steps/s",
-            "cores": blas_threads, "kind": "oracle",
-            "sample": f"extrapolated: {n_layer} oracle layer calls (QKV, attention, FFN) on "
-                      f"{rng_rows} rows ({t_layer:.2f} s each), saliency of {n_tok} tokens over "
-                      f"the full vocabulary, selection of {dims.B} sequences; scaled to "
-                      f"{layer_rows} layer rows and {dims.B * dims.S} scored tokens per step "
-                      f"(float64 numpy, BLAS on {blas_threads} threads, the rest on one)"}
+            "cores": O.threads(), "kind": "oracle",
+            "sample": f"extrapolated: {n_layer} C++ oracle layer calls (QKV + K/V scatter, "
+                      f"attention over every key, FFN + scatter) on {rows} rows ({t_layer:.2f} s "
+                      f"each), saliency of {dims.S} tokens over the full vocabulary "
+                      f"({t_sal:.2f} s), selection of {dims.B} sequences; scaled to {layer_rows} "
+                      f"layer rows and {dims.B * dims.S} scored tokens per step (float64, "
+                      f"std::thread over rows on {O.threads()} threads)"}
 
 
 def run_llada_decode(args):
@@ -953,31 +948,34 @@ def cpu_baseline(one_set, dims, k_sel, budget_s):
 
     import oracle as O
 
-    wd, h_prev, h_cur, logits, kc, vc, h_out = one_set
-    dec = lambda t: O.decode_bf16(t.detach().cpu().contiguous().view(torch.uint16).numpy())  # noqa
-    hp, hc, lg = dec(h_prev[0]), dec(h_cur[0]), dec(logits[0])
-    w = {n: dec(getattr(wd, n)) for n in ("g_attn", "w_qkv", "w_o", "g_ffn", "w_gate", "w_up",
-                                            "w_down")}
-    k0, v0, y0 = dec(kc), dec(vc), dec(h_out)
+    import synth
+
+    # the generator outputs of set 0 (weights, hidden states, logits) as bf16 bit patterns; the
+    # step t-1 caches and hidden rows are fresh synthetic tensors of their shapes (the oracle's
+    # time does not depend on their values)
+    wd, h_prev, h_cur, logits = one_set[:4]
+    bits = lambda t: t.detach().cpu().contiguous().view(torch.uint16).numpy()  # noqa: E731
+    hp, hc, lg = bits(h_prev[0]), bits(h_cur[0]), bits(logits[0])
+    w = {n: bits(getattr(wd, n)) for n in ("g_attn", "w_qkv", "w_o", "g_ffn", "w_gate", "w_up",
+                                             "w_down")}
+    k0 = bits(synth.normal((dims.B, dims.Hkv, dims.S, dims.hd), 1.0, 5101, torch.bfloat16))
+    v0 = bits(synth.normal((dims.B, dims.Hkv, dims.S, dims.hd), 1.0, 5102, torch.bfloat16))
+    y0 = bits(synth.normal((dims.B, dims.S, dims.d), 1.0, 5103, torch.bfloat16))
     scale = 1.0 / math.sqrt(dims.hd)
     steps, t0 = 0, time.perf_counter()
     while True:
         score, _, _ = O.saliency(hc, hp, lg, 0.5)
         sel, rp = O.select_compact(score.reshape(1, -1), None, O.SEL_TOPK, k=k_sel)
-        O.selected_layer(hc[None], w, sel, rp, k0, v0, y0, dims.H, dims.Hkv, dims.hd, 1e-5, scale)
+        O.selected_layer(hc[None], w, sel, rp, k0, v0, y0, dims.H, dims.Hkv, dims.hd, 1e-5, scale,
+                         store="bf16")
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 200:
             break
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max(i.get("num_threads", 1) for i in threadpool_info())
-    except Exception:
-        blas_threads = os.cpu_count()
     return {"value": round(k_sel * steps / el, 2), "unit": "selected-token layer-steps/s",
-            "cores": blas_threads, "kind": "oracle",
-            "sample": f"{steps} whole oracle steps of the same workload (set 0), {el:.1f} s; "
-                      f"float64 numpy, BLAS products on {blas_threads} threads, the rest on one"}
+            "cores": O.threads(), "kind": "oracle",
+            "sample": f"{steps} whole C++ oracle steps of the same workload (set 0), {el:.1f} s; "
+                      f"float64, std::thread over rows on {O.threads()} threads"}
 
 
 if __name__ == "__main__":

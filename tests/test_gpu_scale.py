@@ -6,7 +6,7 @@ recomputes a deterministic sample of rows from the same generator outputs. Rows 
 given their inputs, so a sampled row is compared with its full-size result.
 
 Workloads: LLaDA-8B step (B=8, S=1024, 205 selected per sequence), long context (B=1, S=4096,
-32 forced + 64 selected), Dream-7B GQA (B=16, S=2048, 28/4 heads, 5% and 50% selected).
+32 forced + 64 selected), Dream-7B GQA (B=16, S=2048, 28/4 heads, 5%, 10%, 25% and 50% selected).
 """
 import math
 
@@ -57,6 +57,8 @@ CASES = {
     "llada_step": (W.LLADA_STEP, W.STEP_TOPK),
     "llada_long": (W.LLADA_LONG, 96),
     "dream_5pct": (W.DREAM_GQA, 102),
+    "dream_10pct": (W.DREAM_GQA, 205),
+    "dream_25pct": (W.DREAM_GQA, 512),
     "dream_50pct": (W.DREAM_GQA, 1024),
 }
 
