@@ -42,7 +42,8 @@
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned, row-major and
  *     contiguous with the layouts given below. The library allocates nothing and keeps no mutable
- *     global state; calls are re-entrant.
+ *     global state (except the static device array of dllm_commit_noalloc); calls are
+ *     re-entrant.
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously; no
  *     call synchronises the device.
  *   - All arguments are validated on the host before anything is enqueued. DLLM_ERR_INVALID_ARG,
@@ -287,6 +288,22 @@ dllm_status dllm_commit(const dllm_shape* shape, const void* logits, int32_t pro
                         int32_t block_len, float tau, int32_t k_min, int32_t* tok, int32_t* blk,
                         int32_t* committed_idx, int32_t* committed_rp, uint8_t* flags, void* ws,
                         size_t ws_bytes, void* stream);
+
+/* dllm_commit without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * per-position confidences and token ids of the active blocks live in a static device array of
+ * the library (DLLM_COMMIT_NOALLOC_MAX_ROWS entries of 8 bytes, one copy per GPU, held until the
+ * process ends). Arguments, outputs and errors as dllm_commit, plus DLLM_ERR_WORKSPACE when
+ * shape->B * block_len exceeds DLLM_COMMIT_NOALLOC_MAX_ROWS. The call allocates nothing; its
+ * first call on a device looks up that device's copy of the array (DLLM_ERR_HIP if the lookup
+ * fails). Every call on one GPU shares the array, so calls that overlap on one GPU (on different
+ * streams, or from several host threads without ordering) race; calls ordered on one stream do
+ * not. Each call writes every array entry it reads before reading it. */
+#define DLLM_COMMIT_NOALLOC_MAX_ROWS 65536
+dllm_status dllm_commit_noalloc(const dllm_shape* shape, const void* logits, int32_t prompt_len,
+                                int32_t block_len, float tau, int32_t k_min, int32_t* tok,
+                                int32_t* blk, int32_t* committed_idx, int32_t* committed_rp,
+                                uint8_t* flags, void* stream);
 
 /* Embedding rows of listed positions [the next step's input after a commit]. For
  * j < M = min(row_ptr[B], m_cap), with p = sel_idx[j] (flat b*S + s) and t = tok[p]:

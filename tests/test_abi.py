@@ -227,3 +227,23 @@ def test_commit_and_embed_validation():
     assert rc(e, s, P + 8, P, P, P, P, 128, P) == tsp.DLLM_ERR_INVALID_ARG  # misaligned
     small = tsp.Shape(B=1, S=16, d=4, H=1, Hkv=1, hd=64, F=64, dtype="bf16", V=10)
     assert rc(e, small, P, P, P, P, P, 4, P) == tsp.DLLM_ERR_UNSUPPORTED  # 8-byte rows
+
+
+def test_commit_noalloc_validation():
+    """The allocation-free commit rejects what dllm_commit rejects, and a batch whose active-block
+    rows exceed its static scratch, before touching the device."""
+    lib = tsp.library()
+    s = llada()
+    args = lambda **k: [k.get("shape", s), k.get("logits", P), k.get("prompt", 512),  # noqa: E731
+                        k.get("block", 32), k.get("tau", 0.9), k.get("k", 1), P, P, P, P, P]
+    call = lambda a: lib.dllm_commit_noalloc(ctypes.byref(a[0]), *a[1:], None)  # noqa: E731
+    assert call(args(logits=None)) == tsp.DLLM_ERR_INVALID_ARG
+    assert call(args(block=0)) == tsp.DLLM_ERR_INVALID_ARG
+    assert call(args(tau=float("nan"))) == tsp.DLLM_ERR_INVALID_ARG
+    assert call(args(logits=P + 4)) == tsp.DLLM_ERR_INVALID_ARG
+    assert call(args(block=tsp.MAX_BLOCK_LEN + 1)) == tsp.DLLM_ERR_UNSUPPORTED
+    big = tsp.Shape(B=tsp.COMMIT_NOALLOC_MAX_ROWS // 256 + 1, S=1024, d=4096, H=32, Hkv=32,
+                    hd=128, F=12288, dtype="bf16", V=126464)
+    assert call(args(shape=big, block=256)) == tsp.DLLM_ERR_WORKSPACE
+    with pytest.raises(tsp.DllmError, match="DLLM_ERR_WORKSPACE"):
+        tsp.dllm_commit_noalloc(big, P, 512, 256, 0.9, 1, P, P, P, P, P)

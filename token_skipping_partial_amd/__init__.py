@@ -26,10 +26,12 @@ OP_SALIENCY, OP_SELECT, OP_QKV, OP_ATTN, OP_FFN, OP_COMMIT = range(6)
 MAX_SELECT_S = 8192
 MAX_SALIENT_S = 8192
 MAX_BLOCK_LEN = 256
+COMMIT_NOALLOC_MAX_ROWS = 65536
 
 EXPORTS = ("dllm_saliency", "dllm_select_compact", "dllm_gather_qkv_scatter_kv",
            "dllm_partial_attn", "dllm_gather_ffn_scatter", "dllm_gather_kv_rows",
-           "dllm_salient_attn", "dllm_gather_rows", "dllm_commit", "dllm_embed_rows",
+           "dllm_salient_attn", "dllm_gather_rows", "dllm_commit", "dllm_commit_noalloc",
+           "dllm_embed_rows",
            "dllm_flags_from_rows",
            "dllm_workspace_bytes", "dllm_status_string", "dllm_version")
 
@@ -89,6 +91,7 @@ def _load():
                                     P]),
         "dllm_gather_rows": (I32, [SP, P, I32, P, P, I32, P, P]),
         "dllm_commit": (I32, [SP, P, I32, I32, F, I32, P, P, P, P, P, P, SZ, P]),
+        "dllm_commit_noalloc": (I32, [SP, P, I32, I32, F, I32, P, P, P, P, P, P]),
         "dllm_embed_rows": (I32, [SP, P, P, P, P, P, I32, P, P]),
         "dllm_flags_from_rows": (I32, [SP, P, P, P, I32, P, P]),
         "dllm_workspace_bytes": (SZ, [I32, SP, I32]),
@@ -230,6 +233,15 @@ def dllm_commit(shape, logits, prompt_len, block_len, tau, k_min, tok, blk, comm
                             float(tau), int(k_min), _ptr(tok), _ptr(blk), _ptr(committed_idx),
                             _ptr(committed_rp), _ptr(flags), wp, wn, _stream(stream)),
            "dllm_commit")
+
+
+def dllm_commit_noalloc(shape, logits, prompt_len, block_len, tau, k_min, tok, blk,
+                        committed_idx, committed_rp, flags, stream=None):
+    """dllm_commit with the library's static device scratch instead of a workspace."""
+    _check(_lib.dllm_commit_noalloc(ctypes.byref(shape), _ptr(logits), int(prompt_len),
+                                    int(block_len), float(tau), int(k_min), _ptr(tok), _ptr(blk),
+                                    _ptr(committed_idx), _ptr(committed_rp), _ptr(flags),
+                                    _stream(stream)), "dllm_commit_noalloc")
 
 
 def dllm_embed_rows(shape, emb, mask_emb, tok, sel_idx, row_ptr, m_cap, x, stream=None):

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dllm.h"
 #include "kernels.h"
 
@@ -38,6 +40,29 @@ ProjShape proj_shape(const dllm_shape* s, int32_t m_cap) {
 }
 
 dllm_status hip_status(hipError_t e) { return e == hipSuccess ? DLLM_OK : DLLM_ERR_HIP; }
+
+// Static scratch of dllm_commit_noalloc: confidences, then token ids, of up to
+// DLLM_COMMIT_NOALLOC_MAX_ROWS (sequence, block row) pairs. Every GPU the library runs on holds
+// its own copy at its own address; `scratch` in host code only names the symbol, so the device
+// address is looked up once per device (hipGetSymbolAddress) and only that address is used.
+static __device__ __align__(256) char scratch[(size_t)DLLM_COMMIT_NOALLOC_MAX_ROWS * 8];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of the current device's copy of `scratch` (NULL on a runtime error)
+char* commit_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return static_cast<char*>(g_scratch_ptr[dev]);
+}
 
 dllm_status ws_status(const void* ws, size_t have, size_t need) {
   if (need == 0) return DLLM_OK;
@@ -303,6 +328,35 @@ dllm_status dllm_commit(const dllm_shape* shape, const void* logits, int32_t pro
   const size_t half = (((size_t)shape->B * block_len * 4) + 255) & ~(size_t)255;
   c.conf = (float*)ws;
   c.arg = (int32_t*)((char*)ws + half);
+  return hip_status(launch_commit(shape->dtype == DLLM_BF16, c, (hipStream_t)stream));
+}
+
+dllm_status dllm_commit_noalloc(const dllm_shape* shape, const void* logits, int32_t prompt_len,
+                                int32_t block_len, float tau, int32_t k_min, int32_t* tok,
+                                int32_t* blk, int32_t* committed_idx, int32_t* committed_rp,
+                                uint8_t* flags, void* stream) {
+  if (!base_shape_ok(shape) || !logits || !tok || !blk || !committed_idx || !committed_rp ||
+      !flags || shape->V <= 0 || prompt_len < 0 || prompt_len > shape->S || block_len < 1 ||
+      k_min < 0 || tau != tau || !aligned16(logits))
+    return DLLM_ERR_INVALID_ARG;
+  if (block_len > kMaxBlockLen || shape->V % 8 != 0 || shape->V > 0x7fffffffL)
+    return DLLM_ERR_UNSUPPORTED;
+  const size_t rows = (size_t)shape->B * block_len;
+  if (rows > (size_t)DLLM_COMMIT_NOALLOC_MAX_ROWS) return DLLM_ERR_WORKSPACE;
+  char* base = commit_scratch();
+  if (!base) return DLLM_ERR_HIP;
+  CommitArgs c;
+  c.logits = logits;
+  c.B = shape->B; c.S = shape->S; c.V = shape->V;
+  c.P = prompt_len; c.L = block_len;
+  c.nblk = (shape->S - prompt_len + block_len - 1) / block_len;
+  c.tau = tau; c.k_min = k_min;
+  c.tok = tok; c.blk = blk; c.cidx = committed_idx; c.crp = committed_rp; c.flags = flags;
+  // conf at the start of the array, arg after the conf entries of the maximum row count: the
+  // row-confidence kernel writes both for every (sequence, block row) before the decision
+  // kernel reads them, so no entry needs clearing
+  c.conf = (float*)base;
+  c.arg = (int32_t*)(base + (size_t)DLLM_COMMIT_NOALLOC_MAX_ROWS * 4);
   return hip_status(launch_commit(shape->dtype == DLLM_BF16, c, (hipStream_t)stream));
 }
 
