@@ -252,14 +252,19 @@ static void launch_rmsnorm_rows(const Tin* in, const int32_t* sel_idx, const Tou
 // 2 x 2 waves.
 
 // Tiles of the 32 x 32 x 16 kernel used when more than kWsMaxRows rows are selected: 256 x 256
-// and 128 x 256 (the more tiles, the better they balance over the CUs; plan_g32 chooses). Both
-// use 32-wide K slots in a 4-slot ring and 8 waves (wave tiles 64 x 128 as 4 x 2, and 64 x 64 as
-// 2 x 4).
+// and 128 x 256 (the more tiles, the better they balance over the CUs; plan_g32 chooses), both
+// with 8 waves (wave tiles 64 x 128 as 4 x 2, and 64 x 64 as 2 x 4) and 64-wide K slots, so that
+// every row a direct-to-LDS load touches is one whole 128-byte line (32-wide slots fetch half
+// lines: twice the L1 -> L2 requests for the same bytes, and more time waiting for them). The
+// 256 x 256 tile's slots are 64 KB, so it runs a 2-slot ring; the 128 x 256 tile a 3-slot one.
+// Measured on the 32-layer batched LLaDA-8B step: 39.8 -> 37.9 ms against 32-wide slots in a
+// 4-slot ring (a 4-wave 2 x 2 layout of 128 x 128 wave tiles, half the LDS reads per product,
+// was slower: 38.8 ms).
 struct G32Shape {
   int bm, bn, bk, wm, wn, st;
 };
-constexpr G32Shape kG32Big{256, 256, 32, 4, 2, 4};  // bm, bn, bk, wm, wn, ring slots
-constexpr G32Shape kG32Mid{128, 256, 32, 2, 4, 4};
+constexpr G32Shape kG32Big{256, 256, 64, 4, 2, 2};  // bm, bn, bk, wm, wn, ring slots
+constexpr G32Shape kG32Mid{128, 256, 64, 2, 4, 3};
 
 // ring slots that fit in the 160 KB of LDS a workgroup may use, capped at `want`
 constexpr int ring_slots(int bm, int bn, int bk, int want) {
@@ -528,7 +533,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_bf16_kernel(GemmArgs g, E
   constexpr int SLOT = (BM + BN) * BK * 2;
   constexpr int NMIN = (BM + BN) * BK * 2 / 1024 / NW;  // DMA instructions per wave per slot (lower bound)
   static_assert(MB >= 1 && NB >= 1 && (!SWIGLU || NB % 2 == 0), "tile");
-  static_assert(ST >= 3 && (ST - 2) * NMIN < 64 && NMIN >= 1, "ring depth");
+  static_assert(ST >= 2 && (ST < 3 || (ST - 2) * NMIN < 64) && NMIN >= 1 && NMIN < 64, "ring depth");
   __shared__ __attribute__((aligned(1024))) char ring[ST * SLOT];
 
   const int M = live_rows(g.row_ptr, g.B, g.m_cap);
@@ -603,11 +608,44 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_bf16_kernel(GemmArgs g, E
     if constexpr (P > R) __builtin_amdgcn_sched_group_barrier(0x008, P - R, 0);
   };
 
+  if constexpr (ST == 2) {
+    // Two slots: slot kt+1 loads while slot kt is multiplied. At the last k-step of slot kt
+    // every wave has issued its reads of it; once they have returned (lgkmcnt) and slot kt+1 has
+    // landed (vmcnt), a barrier lets slot kt+2 refill slot kt and the first fragments of slot
+    // kt+1 be read, while the last k-step's products of slot kt run.
+    ISSUE32(ring, kb);
+    if (nk > 1) ISSUE32(ring + SLOT, kb + BK);
+    if (nk > 1) wait_vm<NMIN>(); else wait_vm<0>();
+    wg_barrier();
+    read_frags(ring, 0, xa, wa);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* slot = ring + (kt & 1) * SLOT;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        bf16x8 xn[MB], wn[NB];
+        if (kk + 1 < KS) {
+          read_frags(slot, kk + 1, xn, wn);
+        } else {
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this stage's reads are done
+          wait_vm<0>();                       // stage kt+1 landed
+          wg_barrier();
+          if (kt + 2 < nk) ISSUE32(ring + (kt & 1) * SLOT, kb + (kt + 2) * BK);
+          read_frags(ring + ((kt + 1) & 1) * SLOT, 0, xn, wn);  // stale on the last stage, unused
+        }
+        products(xa, wa);
+        interleave();
+#pragma unroll
+        for (int i = 0; i < MB; ++i) xa[i] = xn[i];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) wa[j] = wn[j];
+      }
+    }
+  } else {
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
     if (s < nk)
       ISSUE32(ring + s * SLOT, kb + s * BK);
-  wait_batches<NMIN, ST - 2>(nk - 1);  // slot 0 landed (slots issued after it: min(ST-2, nk-1))
+  wait_batches<NMIN, (ST >= 2 ? ST - 2 : 0)>(nk - 1);  // slot 0 landed (slots issued after it: min(ST-2, nk-1))
   wg_barrier();
   read_frags(ring, 0, xa, wa);
 
@@ -619,7 +657,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_bf16_kernel(GemmArgs g, E
     interleave();
     if (kt + 1 < nk) {
       // slot kt+1 landed (slots issued after it: min(ST-3, nk-2-kt) + this iteration's none yet)
-      wait_batches<NMIN, ST - 3>(nk - 2 - kt);
+      wait_batches<NMIN, (ST >= 3 ? ST - 3 : 0)>(nk - 2 - kt);
       wg_barrier();  // every wave finished reading slot kt-1
       if (kt + ST - 1 < nk)
         ISSUE32(ring + ((kt + ST - 1) % ST) * SLOT, kb + (kt + ST - 1) * BK);
@@ -645,6 +683,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_bf16_kernel(GemmArgs g, E
     }
   }
 
+  }
 #undef ISSUE32
   // acc[i][j][4 q + r] = C[m = m0 + wm WTM + 32 i + l32][n = n0 + (n-block j) + 8 q + 4 h + r]
 #pragma unroll
