@@ -423,7 +423,7 @@ def run_llada_step(args):
         partial_attn = {"achieved": pa["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(pa["GB/s"] / HBM_PEAK_GBS, 4), "rows": M,
                         "us_per_launch": pa["us_per_launch"],
-                        "kernel": CALL_KERNELS["attn"]}
+                        "kernel": CALL_KERNELS["attn"], "traffic": call_traffic("sel_attn")}
     cpu = None
     if args.cpu_seconds > 0 and not args.second_skip:
         cpu = cpu_baseline_step(dims, L, skip, M, args.cpu_seconds)
