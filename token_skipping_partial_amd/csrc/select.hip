@@ -11,9 +11,12 @@
 // lane its rank, per-wave totals in LDS give the workgroup offset. No atomics touch global
 // memory and no floating-point sum is involved: the result is bit-exact and deterministic.
 //
-// Each workgroup recomputes the selected counts of the sequences before it (a pass over their
-// flag bytes, and over their scores in threshold mode) to find its output offset, so one
-// launch writes sel_idx and row_ptr with no inter-workgroup communication.
+// Each workgroup finds its output offset from the selected counts of the sequences before it, so
+// one launch writes sel_idx and row_ptr with no inter-workgroup communication. A top-k count
+// depends on the flags only: with no flags it is min(k, S) for every sequence (offset b min(k, S),
+// no pass at all); with flags each earlier sequence's flag bytes are counted. In threshold mode
+// the counts of all earlier sequences come from one pass over their flags and scores with a
+// single reduction.
 //
 // Flag byte per position: bit 0 forced (always selected), bit 1 excluded (never a candidate, as
 // the prompt in DyLLM's response-only steps, French summary page §2.C); forced wins.
@@ -51,17 +54,31 @@ __device__ __forceinline__ int pos_state(const SelectArgs& a, size_t i) {
   return (fl & 1) ? 1 : ((fl & 2) ? 2 : 0);
 }
 
-// number of positions sequence r contributes to the output
-__device__ int row_count(const SelectArgs& a, int r, int* scratch) {
-  int nf = 0, nt = 0;  // nf: forced + 65536 * excluded (S <= 8192)
-  for (int s = threadIdx.x; s < a.S; s += kSelThreads) {
-    const int st = pos_state(a, (size_t)r * a.S + s);
-    nf += st == 1 ? 1 : (st == 2 ? 65536 : 0);
-    if (a.mode == 0 && st == 0) nt += a.score[(size_t)r * a.S + s] > a.tau;
+// number of positions sequences 0 .. b-1 contribute to the output
+__device__ int offset_of(const SelectArgs& a, int b, int* scratch) {
+  if (b == 0) return 0;
+  if (a.mode == 1) {
+    if (!a.force) return b * min(a.k, a.S);
+    int base = 0;
+    for (int r = 0; r < b; ++r) {  // per sequence: forced + min(k, candidates)
+      int nf = 0;                  // forced + 65536 * excluded (S <= 8192)
+      for (int s = threadIdx.x; s < a.S; s += kSelThreads) {
+        const int st = pos_state(a, (size_t)r * a.S + s);
+        nf += st == 1 ? 1 : (st == 2 ? 65536 : 0);
+      }
+      nf = block_sum_int(nf, scratch);
+      base += (nf & 65535) + min(a.k, a.S - (nf & 65535) - (nf >> 16));
+    }
+    return base;
   }
-  nf = block_sum_int(nf, scratch);
-  if (a.mode == 0) return (nf & 65535) + block_sum_int(nt, scratch);
-  return (nf & 65535) + min(a.k, a.S - (nf & 65535) - (nf >> 16));
+  // threshold: forced positions plus candidates whose score is above tau, summed over b rows
+  int n = 0;
+  const size_t end = (size_t)b * a.S;
+  for (size_t i = threadIdx.x; i < end; i += kSelThreads) {
+    const int st = pos_state(a, i);
+    n += st == 1 || (st == 0 && a.score[i] > a.tau);
+  }
+  return block_sum_int(n, scratch);
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
@@ -77,8 +94,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S;
 
-  int base = 0;
-  for (int r = 0; r < b; ++r) base += row_count(a, r, scratch);
+  const int base = offset_of(a, b, scratch);
 
   int nfx = 0;  // forced + 65536 * excluded
   for (int s = tid; s < S; s += kSelThreads) {
