@@ -234,7 +234,11 @@ dllm_status dllm_gather_kv_rows(const dllm_shape* shape, const void* k_cache, co
  *                      the new rows put in, against its stored query q_all[p];
  *   o_all[p] = st_o[p] rounded to dtype, for every position.
  * The result for every token is the attention of q_all (after the update) against the updated
- * cache, up to rounding, provided the state held that attention for the previous cache.
+ * cache, up to rounding, provided the state held that attention for the previous cache. An
+ * update that would keep less than a quarter of the token's stored softmax mass (the changed keys
+ * held most of its weight, so the rounding of the removed terms would dominate what is left), or
+ * would give a sum that is not a positive finite number, is not applied: that (token, head) state
+ * is recomputed exactly against every key instead, in a third pass.
  * Initialise the state with a call that selects every position (then nothing is "other").
  * q_first (0 <= q_first <= S) [DyLLM §2.C response-only steps]: unselected positions s < q_first
  * of every sequence are not processed (their query and state are left as they are; o_all there

@@ -215,3 +215,60 @@ def test_response_only_steps_leave_the_prompt_alone(lib):
         o_prev, lse_prev = o_ref, lse_ref
     # after the re-injection step every prompt row is exact again (and stays so in the last step,
     # which changed keys but left the prompt out: the oracle keeps its step-3 rows as well)
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+def test_changed_key_that_held_most_of_the_weight(lib, hd):
+    """A stable token whose attention sat almost wholly (>= 0.9, here about 0.99) on one key that
+    a step changes: the incremental update would subtract nearly all of its stored mass, so the
+    leftover carries the rounding of the removed exponentials magnified by 1 / (1 - w). The
+    library recomputes such a token's state exactly; its context must match the oracle row by
+    row (each row against its own magnitude), in that step and in the next one, which builds on
+    the recomputed state."""
+    B, S, H, Hkv = 1, 160, 2, 2
+    Nq = H * hd
+    scale = 1.0 / math.sqrt(hd)
+    p0, key = 5, 100                       # the stable token and the key it attends to
+    shape = lib.Shape(B=B, S=S, d=Nq, H=H, Hkv=Hkv, hd=hd, F=64, dtype="bf16")
+    q_all = synth.normal((B, S, Nq), 1.0, 840, BF16, "cuda")
+    kc = synth.normal((B, Hkv, S, hd), 1.0, 841, BF16, "cuda")
+    vc = synth.normal((B, Hkv, S, hd), 1.0, 842, BF16, "cuda")
+    for h in range(H):                     # scaled score of about 10 for (p0, h) against `key`
+        qv = q_all[0, p0, h * hd:(h + 1) * hd].float()
+        kc[0, h, key] = (qv * (10.0 / (scale * float(qv.dot(qv))))).to(BF16)
+    qh, kh = host(q_all), host(kc)
+    for h in range(H):
+        z = scale * kh[0, h] @ qh[0, p0, h * hd:(h + 1) * hd]
+        w = np.exp(z - z.max())
+        assert w[key] / w.sum() >= 0.9, "the case must put most of the weight on one key"
+    st_m, st_l, st_o = exact_state(q_all, kc, vc, H, Hkv, hd, scale)
+    o_all = torch.empty(B, S, Nq, dtype=BF16, device="cuda")
+    for t, extra in enumerate([[key, 40, 41], [7, 90, 150]]):
+        print(f"dominant-key step {t}: selected {extra}", flush=True)
+        sel = np.array(sorted(extra), np.int32)
+        rp = np.array([0, len(sel)], np.int32)
+        M = len(sel)
+        sel_d, rp_d = to_dev(sel), to_dev(rp)
+        k_old = torch.empty(M, Hkv, hd, dtype=BF16, device="cuda")
+        v_old = torch.empty_like(k_old)
+        lib.dllm_gather_kv_rows(shape, kc, vc, sel_d, rp_d, M, k_old, v_old)
+        bs = torch.zeros(M, dtype=torch.long, device="cuda")
+        ss = torch.from_numpy(sel).long().cuda()
+        kc[bs, :, ss, :] = synth.normal((M, Hkv, hd), 1.0, 850 + t, BF16, "cuda")
+        vc[bs, :, ss, :] = synth.normal((M, Hkv, hd), 1.0, 860 + t, BF16, "cuda")
+        q_sel = synth.normal((M, Nq), 1.0, 870 + t, BF16, "cuda")
+        q_before = q_all.clone()
+        o_sel = torch.empty(M, Nq, dtype=BF16, device="cuda")
+        lib.dllm_salient_attn(shape, scale, q_sel, q_all, kc, vc, k_old, v_old, sel_d, rp_d, M,
+                              st_m, st_l, st_o, o_sel, o_all, lib.workspace(lib.OP_ATTN, shape, M))
+        torch.cuda.synchronize()
+        _, o_ref, lse_ref = O.salient_attention(host(q_sel), host(q_before), host(kc), host(vc),
+                                                sel, rp, H, Hkv, hd, scale)
+        got, got_st = host(o_all), host(st_o)
+        for h in range(H):
+            cols = slice(h * hd, (h + 1) * hd)
+            assert_close(got[0, p0, cols], o_ref[0, p0, cols], TOL[BF16], f"step {t} token row h{h}")
+            assert_close(got_st[0, p0, cols], o_ref[0, p0, cols], TOL[BF16], f"step {t} state row h{h}")
+        assert_close(got, o_ref, TOL[BF16], f"step {t} o_all")
+        lse = (host(st_m) + np.log2(host(st_l))) * LN2
+        assert_close(lse, lse_ref, 1e-3, f"step {t} log-sum-exp")

@@ -30,6 +30,7 @@ namespace dllm {
 
 constexpr int kTK = 64;         // keys per tile
 constexpr float kLazy = 8.f;    // reference-point slack (base-2 units) before rescaling
+constexpr float kKeepMass = 0.25f;  // stable-token update: smallest kept share of the stored mass
 
 struct AttnArgs {
   const uint16_t* q;
@@ -208,7 +209,11 @@ struct VtFrag<64> {
 // the softmax numerator and denominator relative to the token's stored reference point; the
 // epilogue adds it to the stored state. Rows of selected positions are computed too and are
 // overwritten by the exact pass that runs next.
-template <int HD, int NW, int ST, bool DELTA>
+//
+// FULL: launch-class tag, true when the call has room for every position of every sequence as a
+// query row (m_cap >= B S: the dense layers). The code is the same; the separate instantiation
+// lets kernel traces tell the dense and the selected-row launches apart.
+template <int HD, int NW, int ST, bool DELTA, bool FULL = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr int KK = HD / 16;              // 16-wide k-steps of q.k over hd
@@ -549,6 +554,16 @@ void attn_bf16_kernel(AttnArgs a) {
     const size_t sh = (size_t)qj * a.H + qh;
     const float lf = a.st_l[sh] * fast_exp2(m_state - m_run);
     const float l_new = lf + l_tot;
+    // Cancellation guard. The old rows' exponentials are taken out of the numerator in bf16, so
+    // its error is about 2^-9 of the removed mass, which is at most lf; relative to the result
+    // that is 2^-9 lf / l_new. Where less than a quarter of the stored mass is left (a changed key
+    // held most of the token's weight), or the sum is not a positive finite number, the update
+    // is not used: the state is marked (st_l = -1) and the recompute pass that runs after the
+    // exact pass rebuilds it against every key. Both lanes of a query hold the same sums.
+    if (!(l_new > 0.f && l_new >= kKeepMass * lf && l_new < INFINITY)) {
+      if (h == 0) a.st_l[sh] = -1.f;
+      return;
+    }
     const float inv = 1.0f / l_new;
     float* so = a.st_o + (size_t)qj * Nq + qh * HD;
 #pragma unroll
@@ -720,7 +735,10 @@ static inline int cdiv(long x, long y) { return (int)((x + y - 1) / y); }
 // bf16 launch plan: waves per workgroup (32 query rows each) and the key split. Eight waves
 // (256 rows; at hd 128 one workgroup per CU with a 4-slot ring of 128 KB); at hd 64 four waves
 // (two workgroups per CU) when a (sequence, kv head) has at most 160 query rows on average. The
-// key range is split until the workgroups fill every CU slot, keeping at least 128 keys per split.
+// key range is split until the workgroups fill every CU slot, keeping at least 256 keys (four
+// tiles) per split: with two tiles most of a split's time is the ring's start-up. Measured on
+// MI355X at 128 query rows of one sequence (S = 1024, 32 heads of 128): four waves per workgroup
+// instead of eight 19.7 vs 18.8 us; at least four tiles per split 17.8 vs 19.7 us.
 struct AttnCfg {
   int nw, st, nsplit, kps;
 };
@@ -730,10 +748,10 @@ static AttnCfg plan_bf16(const ProjShape& s) {
   const long rows_avg = (long)cdiv((long)s.m_plan * G, s.B);
   c.nw = (s.hd == 128 || rows_avg > 160) ? 8 : 4;
   c.st = 4;
-  const long slots = 256L * ((c.nw == 8 && s.hd == 128) ? 1 : 2);
+  const long slots = 256L * (s.hd == 128 ? 1 : 2);
   const long est = (long)s.B * s.Hkv * (rows_avg > 0 ? cdiv(rows_avg, 32 * c.nw) : 1);
   c.nsplit = 1;
-  while (est * c.nsplit < slots && s.S / (c.nsplit * 2) >= 128) c.nsplit *= 2;
+  while (est * c.nsplit < slots && s.S / (c.nsplit * 2) >= 256) c.nsplit *= 2;
   c.kps = cdiv(cdiv(s.S, c.nsplit), kTK) * kTK;
   c.nsplit = cdiv(s.S, c.kps);  // every split owns at least one key
   return c;
@@ -751,15 +769,15 @@ size_t attn_workspace_bytes(bool bf16, const ProjShape& s) {
   return ((rows * s.hd * 4 + 255) & ~(size_t)255) + rows * 2 * 4;
 }
 
-template <int HD>
+template <int HD, bool FULL>
 static void launch_bf16(const AttnCfg& c, dim3 grid, const AttnArgs& a, hipStream_t st) {
   if constexpr (HD == 64) {
     if (c.nw == 4) {
-      hipLaunchKernelGGL((attn_bf16_kernel<HD, 4, 4, false>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<HD, 4, 4, false, FULL>), grid, dim3(256), 0, st, a);
       return;
     }
   }
-  hipLaunchKernelGGL((attn_bf16_kernel<HD, 8, 4, false>), grid, dim3(512), 0, st, a);
+  hipLaunchKernelGGL((attn_bf16_kernel<HD, 8, 4, false, FULL>), grid, dim3(512), 0, st, a);
 }
 
 template <int HD>
@@ -816,10 +834,11 @@ static hipError_t launch_exact_bf16(const ProjShape& s, float scale, const void*
   const int G = s.H / s.Hkv;
   const int rows_max = (s.m_cap < s.S ? s.m_cap : s.S) * G;
   dim3 grid(s.B * s.Hkv * a.nsplit, cdiv(rows_max, 32 * c.nw));
+  const bool full = (long)s.m_cap >= (long)s.B * s.S;
   if (s.hd == 64)
-    launch_bf16<64>(c, grid, a, st);
+    full ? launch_bf16<64, true>(c, grid, a, st) : launch_bf16<64, false>(c, grid, a, st);
   else
-    launch_bf16<128>(c, grid, a, st);
+    full ? launch_bf16<128, true>(c, grid, a, st) : launch_bf16<128, false>(c, grid, a, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const size_t threads = (size_t)s.m_cap * s.H * (s.hd / 4);
@@ -848,9 +867,88 @@ __global__ __launch_bounds__(256) void state_context_kernel(const float* st_o, u
   Elem<uint16_t>::store4(o_all + off, v);
 }
 
+// Exact state of the (token, head) pairs the stable-token update marked (st_l < 0, or not a
+// number: a state that no update may build on), against every key of the updated cache with the
+// token's stored query: the definition of the state written out, in float32 with exact
+// exponentials. One workgroup per 256 pairs; it lists its marked pairs in LDS and works through
+// them one at a time with all its threads: scores (a thread per key), maximum and sum, then the
+// context (a thread per (column, key residue) with a fixed-order sum of the residues). Positions
+// before q_first are never touched. A workgroup with no marked pair only reads its 256 sums.
+template <int HD>
+__global__ __launch_bounds__(256) void stable_recompute_kernel(AttnArgs a) {
+  constexpr int KG = 256 / HD;  // key residues of the context sums
+  __shared__ float sc[kSalientMaxS];
+  __shared__ float qs[HD];
+  __shared__ float part[KG][HD];
+  __shared__ float red[4];
+  __shared__ int list[256];
+  __shared__ int nlist;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Nq = a.H * HD, G = a.H / a.Hkv;
+  const size_t total = (size_t)a.B * a.S * a.H;
+  const size_t pair = (size_t)blockIdx.x * 256 + tid;
+  if (tid == 0) nlist = 0;
+  __syncthreads();
+  if (pair < total) {
+    const int s = (int)((pair / a.H) % a.S);
+    if (s >= a.q_first && !(a.st_l[pair] >= 0.f)) list[atomicAdd(&nlist, 1)] = tid;
+  }
+  __syncthreads();
+  const int n = nlist;
+  for (int f = 0; f < n; ++f) {
+    const size_t pr = (size_t)blockIdx.x * 256 + list[f];
+    const size_t pos = pr / a.H;
+    const int h = (int)(pr - pos * a.H), b = (int)(pos / a.S), hk = h / G;
+    const uint16_t* kb = a.kc + ((size_t)b * a.Hkv + hk) * (size_t)a.S * HD;
+    const uint16_t* vb = a.vc + ((size_t)b * a.Hkv + hk) * (size_t)a.S * HD;
+    if (tid < HD) qs[tid] = bf2f(a.q_all[pos * Nq + (size_t)h * HD + tid]);
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int t = tid; t < a.S; t += 256) {
+      float d = 0.f;
+      for (int e = 0; e < HD; ++e) d = fmaf(qs[e], bf2f(kb[(size_t)t * HD + e]), d);
+      sc[t] = d * a.scale_log2;
+      mx = fmaxf(mx, sc[t]);
+    }
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float ls = 0.f;
+    for (int t = tid; t < a.S; t += 256) {
+      const float pt = exp2f(sc[t] - m);
+      sc[t] = pt;
+      ls += pt;
+    }
+    ls = wave_sum(ls);
+    if (lane == 0) red[wave] = ls;
+    __syncthreads();
+    const float l = (red[0] + red[1]) + (red[2] + red[3]);
+    const int e = tid % HD, g = tid / HD;
+    float acc = 0.f;
+    for (int t = g; t < a.S; t += KG) acc = fmaf(sc[t], bf2f(vb[(size_t)t * HD + e]), acc);
+    part[g][e] = acc;
+    __syncthreads();
+    if (tid < HD) {
+      float o = 0.f;
+      for (int k = 0; k < KG; ++k) o += part[k][tid];
+      o /= l;
+      a.st_o[pos * Nq + (size_t)h * HD + tid] = o;
+      a.o_all[pos * Nq + (size_t)h * HD + tid] = f2bf(o);
+    }
+    if (tid == 0) {
+      a.st_m[pr] = m;
+      a.st_l[pr] = l;
+    }
+    __syncthreads();  // qs, sc and part are rewritten for the next pair
+  }
+}
+
 // DyLLM (French summary page) §2.B: stable tokens reuse their previous attention weights and take
 // in only the changed keys (pass 1, every position), salient tokens are recomputed exactly against
-// the updated cache (pass 2, the selected rows; it overwrites what pass 1 wrote at their positions).
+// the updated cache (pass 2, the selected rows; it overwrites what pass 1 wrote at their positions);
+// the stable tokens whose update pass 1 declined are recomputed exactly (pass 3).
 hipError_t launch_salient_attn(const ProjShape& s, float scale, const void* q_sel, void* q_all,
                                const void* k_cache, const void* v_cache, const void* k_old,
                                const void* v_old, const int32_t* sel_idx, const int32_t* row_ptr,
@@ -886,8 +984,18 @@ hipError_t launch_salient_attn(const ProjShape& s, float scale, const void* q_se
     else hipLaunchKernelGGL((attn_bf16_kernel<128, 4, 4, true>), grid, dim3(256), 0, st, d);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || s.m_cap == 0) return e;
-  return launch_exact_bf16(s, scale, q_sel, k_cache, v_cache, row_ptr, o_sel, ws, d, st);
+  if (e != hipSuccess) return e;
+  if (s.m_cap > 0) {
+    e = launch_exact_bf16(s, scale, q_sel, k_cache, v_cache, row_ptr, o_sel, ws, d, st);
+    if (e != hipSuccess) return e;
+  }
+  if (rows == 0) return hipSuccess;
+  const dim3 rg(cdiv((long)s.B * s.S * s.H, 256));
+  if (s.hd == 64)
+    hipLaunchKernelGGL(stable_recompute_kernel<64>, rg, dim3(256), 0, st, d);
+  else
+    hipLaunchKernelGGL(stable_recompute_kernel<128>, rg, dim3(256), 0, st, d);
+  return hipGetLastError();
 }
 
 // copies of the K/V rows at the selected positions: rows[j, hk, :] = cache[b, hk, s, :]
