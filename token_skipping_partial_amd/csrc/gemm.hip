@@ -43,6 +43,32 @@ struct FastDiv {
   __device__ __forceinline__ uint32_t div(uint32_t n) const { return (__umulhi(m, n) + n) >> l; }
 };
 
+// Epilogues run in two phases per block of rows: pre(row, n) issues the loads a group of 4 output
+// columns needs and returns them as loaded (no conversion, so nothing waits for them yet);
+// operator()(row, n, v, pre) combines and stores. A kernel issues every pre() of a row block
+// before its first store, so the block pays one memory latency instead of one per group.
+struct NoPre {};
+template <typename T> struct Raw4;  // 4 consecutive elements as loaded
+template <> struct Raw4<float> {
+  typedef float4 type;
+  __device__ __forceinline__ static float4 load(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+  }
+  __device__ __forceinline__ static void cvt(const float4& r, float a[4]) {
+    a[0] = r.x; a[1] = r.y; a[2] = r.z; a[3] = r.w;
+  }
+};
+template <> struct Raw4<uint16_t> {  // bf16 bit patterns
+  typedef uint2 type;
+  __device__ __forceinline__ static uint2 load(const uint16_t* p) {
+    return *reinterpret_cast<const uint2*>(p);
+  }
+  __device__ __forceinline__ static void cvt(const uint2& r, float a[4]) {
+    a[0] = __uint_as_float(r.x << 16); a[1] = __uint_as_float(r.x & 0xffff0000u);
+    a[2] = __uint_as_float(r.y << 16); a[3] = __uint_as_float(r.y & 0xffff0000u);
+  }
+};
+
 template <typename T>
 struct EpiQKV {  // Q -> q_sel[j]; K/V -> cache[b, hk, s, e] of the token's own position
   T* q_sel;
@@ -74,6 +100,11 @@ struct EpiQKV {  // Q -> q_sel[j]; K/V -> cache[b, hk, s, e] of the token's own 
     const int hk = kv >> hd_log2, e = kv & ((1 << hd_log2) - 1);
     Elem<T>::store4(cache + r.kv + (((size_t)hk * S) << hd_log2) + e, v);
   }
+  typedef NoPre Pre;
+  __device__ __forceinline__ Pre pre(const Row&, int) const { return {}; }
+  __device__ __forceinline__ void operator()(const Row& r, int n, const float v[4], Pre) const {
+    (*this)(r, n, v);
+  }
 };
 
 template <typename T>
@@ -89,11 +120,17 @@ struct EpiResidF32 {  // h[j] = h_in[sel[j]] + acc  (float32 workspace)
   __device__ __forceinline__ Row row(int j) const {
     return Row{h + (size_t)j * d, x + (size_t)sel_idx[j] * d};
   }
-  __device__ __forceinline__ void operator()(const Row& r, int n, const float v[4]) const {
+  typedef typename Raw4<T>::type Pre;
+  __device__ __forceinline__ Pre pre(const Row& r, int n) const { return Raw4<T>::load(r.x + n); }
+  __device__ __forceinline__ void operator()(const Row& r, int n, const float v[4],
+                                             const Pre& p) const {
     float a[4];
-    Elem<T>::load4(r.x + n, a);
+    Raw4<T>::cvt(p, a);
     const float o[4] = {v[0] + a[0], v[1] + a[1], v[2] + a[2], v[3] + a[3]};
     Elem<float>::store4(r.h + n, o);
+  }
+  __device__ __forceinline__ void operator()(const Row& r, int n, const float v[4]) const {
+    (*this)(r, n, v, pre(r, n));
   }
 };
 
@@ -110,11 +147,17 @@ struct EpiResidScatter {  // h_out[sel[j]] = h[j] + acc
   __device__ __forceinline__ Row row(int j) const {
     return Row{h_out + (size_t)sel_idx[j] * d, h + (size_t)j * d};
   }
-  __device__ __forceinline__ void operator()(const Row& r, int n, const float v[4]) const {
+  typedef float4 Pre;
+  __device__ __forceinline__ Pre pre(const Row& r, int n) const { return Raw4<float>::load(r.h + n); }
+  __device__ __forceinline__ void operator()(const Row& r, int n, const float v[4],
+                                             const Pre& p) const {
     float a[4];
-    Elem<float>::load4(r.h + n, a);
+    Raw4<float>::cvt(p, a);
     const float o[4] = {v[0] + a[0], v[1] + a[1], v[2] + a[2], v[3] + a[3]};
     Elem<T>::store4(r.out + n, o);
+  }
+  __device__ __forceinline__ void operator()(const Row& r, int n, const float v[4]) const {
+    (*this)(r, n, v, pre(r, n));
   }
 };
 
@@ -130,6 +173,12 @@ struct EpiSwiGLU {  // z[j, n] = silu(gate) * up
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = g[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[i])) * u[i];
     Elem<T>::store4(r + n, o);
+  }
+  typedef NoPre Pre;
+  __device__ __forceinline__ Pre pre(Row, int) const { return {}; }
+  __device__ __forceinline__ void operator()(Row r, int n, const float g[4], const float u[4],
+                                             Pre) const {
+    (*this)(r, n, g, u);
   }
 };
 
@@ -426,38 +475,71 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g, Epi
   }
 
   // acc[i][j][r] = C[m = m0 + wm WTM + 16 i + lr][n = n0 + (n-block j) + 4 lc + r]
+  // Per 16-row block: the epilogue's loads first, then the masked stores, with the branches
+  // outside the store sequences (as in the 32 x 32 x 16 kernel's epilogue).
+  constexpr int NJ = SWIGLU ? NB / 2 : NB;
+  const bool cols_in = n0 + (SWIGLU ? BN / 2 : BN) <= g.N;
+  auto col = [&](int j) __attribute__((always_inline)) {
+    return n0 + wrow<BN, WN, NB, SWIGLU>(wn, j) + 4 * lc;
+  };
+  auto gate = [&](int i, int j, float (&v)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r];
+  };
+  if (g.partial) {  // K-split partials: [split][row][N] ([split][row][gate 0..N | up N..2N])
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int m = m0 + wm * WTM + 16 * i + lr;
+      if (m >= M) continue;
+      float* pr = g.partial + ((size_t)blockIdx.z * g.m_cap + m) * ((SWIGLU ? 2 : 1) * (size_t)g.N);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int n = col(j);
+        if (!cols_in && n >= g.N) continue;
+        float v[4];
+        gate(i, j, v);
+        Elem<float>::store4(pr + n, v);
+        if constexpr (SWIGLU) {
+          gate(i, j + NB / 2, v);
+          Elem<float>::store4(pr + g.N + n, v);
+        }
+      }
+    }
+    return;
+  }
+  decltype(epi.row(0)) ers[MB];  // row addresses of every block before the first store
+#pragma unroll
+  for (int i = 0; i < MB; ++i) ers[i] = epi.row(min(m0 + wm * WTM + 16 * i + lr, M - 1));
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int m = m0 + wm * WTM + 16 * i + lr;
-    if (m >= M) continue;
-    const auto er = epi.row(m);
-    if constexpr (SWIGLU) {
+    const auto& er = ers[i];
+    typename Epi::Pre pre[NJ];
 #pragma unroll
-      for (int j = 0; j < NB / 2; ++j) {
-        const int n = n0 + wrow<BN, WN, NB, true>(wn, j) + 4 * lc;
-        if (n >= g.N) continue;
-        const float gv[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-        const float uv[4] = {acc[i][j + NB / 2][0], acc[i][j + NB / 2][1],
-                             acc[i][j + NB / 2][2], acc[i][j + NB / 2][3]};
-        if (g.partial) {  // [split][row][gate 0..N | up N..2N]
-          float* pr = g.partial + ((size_t)blockIdx.z * g.m_cap + m) * (2 * (size_t)g.N);
-          Elem<float>::store4(pr + n, gv);
-          Elem<float>::store4(pr + g.N + n, uv);
-        } else {
-          epi(er, n, gv, uv);
-        }
+    for (int j = 0; j < NJ; ++j) {
+      const int n = col(j);
+      pre[j] = epi.pre(er, (cols_in || n < g.N) ? n : 0);
+    }
+    if (m >= M) continue;
+    auto store = [&](int j) __attribute__((always_inline)) {
+      const int n = col(j);
+      float v[4];
+      gate(i, j, v);
+      if constexpr (SWIGLU) {
+        float u[4];
+        gate(i, j + NB / 2, u);
+        epi(er, n, v, u, pre[j]);
+      } else {
+        epi(er, n, v, pre[j]);
       }
+    };
+    if (cols_in) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) store(j);
     } else {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = n0 + wrow<BN, WN, NB, false>(wn, j) + 4 * lc;
-        if (n >= g.N) continue;
-        const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-        if (g.partial)
-          Elem<float>::store4(g.partial + ((size_t)blockIdx.z * g.m_cap + m) * g.N + n, v);
-        else
-          epi(er, n, v);
-      }
+      for (int j = 0; j < NJ; ++j)
+        if (col(j) < g.N) store(j);
     }
   }
 }
@@ -686,44 +768,84 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_bf16_kernel(GemmArgs g, E
   }
 #undef ISSUE32
   // acc[i][j][4 q + r] = C[m = m0 + wm WTM + 32 i + l32][n = n0 + (n-block j) + 8 q + 4 h + r]
+  // Per 32-row block: every load the epilogue needs is issued first (rows past M load row M-1,
+  // columns past N column 0), then the stores, masked to the rows below M (and, when the tile
+  // reaches past N, to the columns below it). The branches are uniform and sit outside the
+  // store sequences, so each store waits only for its own loads (on gfx9 stores count against
+  // the same counter as loads: a wait placed at a branch join would wait for every earlier
+  // store too).
+  constexpr int NJ = SWIGLU ? NB / 2 : NB;
+  const bool cols_in = n0 + (SWIGLU ? BN / 2 : BN) <= g.N;
+  auto col = [&](int q, int j) __attribute__((always_inline)) {
+    return n0 + wrow32<BN, WN, NB, SWIGLU>(wn, j) + 8 * q + 4 * h;
+  };
+  auto gate = [&](int i, int j, int q, float (&v)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+  };
+  if (g.partial) {  // K-split partials: [split][row][N] ([split][row][gate 0..N | up N..2N])
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int m = m0 + wm * WTM + 32 * i + l32;
+      if (m >= M) continue;
+      float* pr = g.partial + ((size_t)blockIdx.z * g.m_cap + m) * ((SWIGLU ? 2 : 1) * (size_t)g.N);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int n = col(q, j);
+          if (!cols_in && n >= g.N) continue;
+          float v[4];
+          gate(i, j, q, v);
+          Elem<float>::store4(pr + n, v);
+          if constexpr (SWIGLU) {
+            gate(i, j + NB / 2, q, v);
+            Elem<float>::store4(pr + g.N + n, v);
+          }
+        }
+    }
+    return;
+  }
+  // the rows' addresses (which may load an index) for every block before the first store
+  decltype(epi.row(0)) ers[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) ers[i] = epi.row(min(m0 + wm * WTM + 32 * i + l32, M - 1));
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int m = m0 + wm * WTM + 32 * i + l32;
-    if (m >= M) continue;
-    const auto er = epi.row(m);
+    const auto& er = ers[i];
+    typename Epi::Pre pre[4][NJ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if constexpr (SWIGLU) {
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int j = 0; j < NB / 2; ++j) {
-          const int n = n0 + wrow32<BN, WN, NB, true>(wn, j) + 8 * q + 4 * h;
-          if (n >= g.N) continue;
-          const float gv[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                               acc[i][j][4 * q + 3]};
-          const int ju = j + NB / 2;
-          const float uv[4] = {acc[i][ju][4 * q], acc[i][ju][4 * q + 1], acc[i][ju][4 * q + 2],
-                               acc[i][ju][4 * q + 3]};
-          if (g.partial) {  // [split][row][gate 0..N | up N..2N]
-            float* pr = g.partial + ((size_t)blockIdx.z * g.m_cap + m) * (2 * (size_t)g.N);
-            Elem<float>::store4(pr + n, gv);
-            Elem<float>::store4(pr + g.N + n, uv);
-          } else {
-            epi(er, n, gv, uv);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int n = n0 + wrow32<BN, WN, NB, false>(wn, j) + 8 * q + 4 * h;
-          if (n >= g.N) continue;
-          const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                              acc[i][j][4 * q + 3]};
-          if (g.partial)
-            Elem<float>::store4(g.partial + ((size_t)blockIdx.z * g.m_cap + m) * g.N + n, v);
-          else
-            epi(er, n, v);
-        }
+      for (int j = 0; j < NJ; ++j) {
+        const int n = col(q, j);
+        pre[q][j] = epi.pre(er, (cols_in || n < g.N) ? n : 0);
       }
+    if (m >= M) continue;
+    auto store = [&](int q, int j) __attribute__((always_inline)) {
+      const int n = col(q, j);
+      float v[4];
+      gate(i, j, q, v);
+      if constexpr (SWIGLU) {
+        float u[4];
+        gate(i, j + NB / 2, q, u);
+        epi(er, n, v, u, pre[q][j]);
+      } else {
+        epi(er, n, v, pre[q][j]);
+      }
+    };
+    if (cols_in) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) store(q, j);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          if (col(q, j) < g.N) store(q, j);
     }
   }
 }
