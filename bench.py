@@ -339,7 +339,10 @@ def run_llada_step(args):
     """32 LLaDA-8B layers, B=8, S=1024: layers 0-3 on every token, saliency at layer 4 (alpha 0.5,
     fresh previous-step logits), top-205 per sequence, layers 4-31 on the selected rows against the
     cached K/V. Hidden input X^t = X^(t-1) + per-step perturbation; caches carried across steps.
-    The timed region holds the steps back to back with an event at every call boundary."""
+    The timed region holds the steps back to back with an event before and after it (value,
+    ms_per_step). The per-call figures (calls, roofline, partial_attn) come from the next `steps`
+    steps, run the same way with an event at every call boundary: those events cost GPU time of
+    their own, so they stay out of the step time."""
     import synth
     import token_skipping_partial_amd as tsp
     from synth import workloads as W
@@ -356,7 +359,7 @@ def run_llada_step(args):
     k2 = (args.second_k or k_sel // 2) if args.second_skip else 0
     model = EarlySkipModel(shape, layers, skip, SelectConfig(mode=tsp.SEL_TOPK, k=k_sel, alpha=0.5),
                            m_cap=dims.B * k_sel, skip2=args.second_skip, k2=k2)
-    nsteps = args.warmup + args.steps
+    nsteps = args.warmup + 2 * args.steps
     xs = [synth.normal((dims.B, dims.S, dims.d), 1.0, 7500, torch.bfloat16, "cuda")]
     for t in range(1, nsteps + 1):
         large = synth.large_positions(dims.B, dims.S, W.LLADA_LARGE, seed=7600 + t, device="cuda")
@@ -369,17 +372,27 @@ def run_llada_step(args):
     torch.cuda.synchronize()
     print("[bench] warm; timing", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
-    marks = [CallMarks(stream, 8 * L + 16) for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for t in range(args.steps):
         i = args.warmup + t
-        marks[t].start()
-        model.step(xs[1 + i], logits[i % 4], mark=marks[t])
+        model.step(xs[1 + i], logits[i % 4])
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    print(f"[bench] {ms:.3f} ms per step; per-call pass", file=sys.stderr, flush=True)
+    marks = [CallMarks(stream, 8 * L + 16) for _ in range(args.steps)]
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    m0.record(stream)
+    for t in range(args.steps):
+        i = args.warmup + args.steps + t
+        marks[t].start()
+        model.step(xs[1 + i], logits[i % 4], mark=marks[t])
+    m1.record(stream)
+    torch.cuda.synchronize()
+    ms_marked = m0.elapsed_time(m1) / args.steps
     M = int(model.step1.row_ptr[-1].item())
     skip2 = args.second_skip or L
     M2 = int(model.step2.row_ptr[-1].item()) if args.second_skip else M
@@ -437,7 +450,8 @@ def run_llada_step(args):
         "config": {"workload": "llada_step: 32 LLaDA-8B-shaped layers, B=8, S=1024, d=4096, 32x128 "
                                "MHA, FFN 12288, V=126464, early skip at layer 4, alpha=0.5, "
                                "top-205 per sequence",
-                   "units_per_step": units, "selected_per_step": M},
+                   "units_per_step": units, "selected_per_step": M,
+                   "ms_per_step_with_call_events": round(ms_marked, 3)},
         "roofline": roofline,
         "partial_attn": partial_attn,
         "calls": calls,

@@ -737,8 +737,9 @@ static inline int cdiv(long x, long y) { return (int)((x + y - 1) / y); }
 // (two workgroups per CU) when a (sequence, kv head) has at most 160 query rows on average. The
 // key range is split until the workgroups fill every CU slot, keeping at least 256 keys (four
 // tiles) per split: with two tiles most of a split's time is the ring's start-up. Measured on
-// MI355X at 128 query rows of one sequence (S = 1024, 32 heads of 128): four waves per workgroup
-// instead of eight 19.7 vs 18.8 us; at least four tiles per split 17.8 vs 19.7 us.
+// MI355X at 128 query rows of one sequence (S = 1024, 32 heads of 128), us per call: eight waves
+// with at least two / four tiles per split 18.8 / 16.2; four waves (one 128-row tile per
+// sequence and kv head) 19.7 / 17.8.
 struct AttnCfg {
   int nw, st, nsplit, kps;
 };
