@@ -1,27 +1,31 @@
-"""Whole-step parity of the batched LLaDA-8B step at its full shape, teacher-forced per layer.
+"""Whole-step parity of the multi-layer workloads at their full shape, teacher-forced per layer.
 
-The step: 32 layers (d = 4096, 32 x 128 MHA, FFN 12288), B = 8, S = 1024, layers 0-3 on every
-token, saliency of layer 4's input against its previous-step value blended with the previous
-step's max-softmax confidence over the 126464-entry vocabulary (alpha = 0.5), top-205 per
-sequence, layers 4-31 on those rows against the cached K/V (ES-dLLM, German summary page,
-§2.A equation and §2.B). The GPU runs a fill step and two early-skip steps with every cache
-carried.
+Three steps at the shapes of the workloads they stand for, each a fill step (every layer on
+every token) and two early-skip steps with every cache carried (ES-dLLM, German summary page,
+§2.A equation and §2.B; SlowFast, German summary page, for the forced active block):
+  * the batched LLaDA-8B step: 32 layers (d = 4096, 32 x 128 MHA, FFN 12288), B = 8, S = 1024,
+    alpha 0.5 against the full 126464-entry vocabulary, top-205 per sequence;
+  * the Dream-7B GQA step: 28 layers (d = 3584, 28 query heads on 4 kv heads, FFN 18944),
+    B = 16, S = 2048, alpha 0, top-10% and top-25% per sequence;
+  * long-context block decoding: 32 LLaDA-8B layers, B = 1, S = 4096, the active block of 32
+    forced plus the top-64 by change.
 
-After each step the oracle checks, for two of the eight sequences:
-  * the selection: the oracle's scores from the library's own stored bf16 inputs of layer 4
-    (this step's and the previous step's) and the logits, top-205 bit-identical to the
-    library's rows, every score at least 1e-4 from the boundary;
-  * every layer (dense and selected): sampled rows recomputed by the oracle from the library's
-    stored bf16 input of that layer and the layer's K/V cache after the step (the other selected
-    rows' new K/V entries are the library's), rounding to bf16 where the library stores bf16;
-    the rows' K/V cache entries and output hidden rows must agree within the bf16 tolerance.
-Teacher forcing keeps the check at full size affordable (the oracle computes 16 rows per layer,
-not 8192) while every layer of the real shape, caches and selection of each step take part.
+After each step the oracle checks, for one or two sequences:
+  * the selection: the oracle's scores from the library's own stored bf16 inputs of the skip
+    layer (this step's and the previous step's) and the logits, the top-k bit-identical to the
+    library's rows, every candidate score at least 1e-4 from the boundary;
+  * every layer (dense and selected): 8 sampled rows per sequence recomputed by the oracle from
+    the library's stored bf16 input of that layer and the layer's K/V cache after the step (the
+    other selected rows' new K/V entries are the library's), rounding to bf16 where the library
+    stores bf16; the rows' K/V cache entries and output hidden rows must agree within the bf16
+    tolerance.
+Teacher forcing keeps the check at full size affordable (the oracle computes 8-16 rows per
+layer, not thousands) while every layer of the real shape, caches and selection take part.
 
 Inputs: one set of random N(0, 0.02^2) weights for all layers (non-unit norm gains), X0 N(0, 1),
-per step 154 tokens per sequence moved by N(0, 0.5^2) and the rest by N(0, (1e-3)^2); logits
-N(0, 1) with one logit raised by 30 on 51 other tokens per sequence, so the top-205 are those
-205 tokens by a wide margin.
+per step the moving tokens (154, k or 64 per sequence) moved by N(0, 0.5^2) and the rest by
+N(0, (1e-3)^2); for the LLaDA step logits N(0, 1) with one logit raised by 30 on 51 other tokens
+per sequence, so the top-205 are those 205 tokens by a wide margin.
 """
 import math
 
@@ -51,24 +55,74 @@ def topk_margin(score, k):
     return float(np.min(np.abs(score - thr[:, None])))
 
 
-def test_llada_step_full_shape_teacher_forced(lib):
-    from token_skipping_partial_amd.step import EarlySkipModel, LayerWeights, SelectConfig
+def shared_weights(dims, seed):
+    w = synth.layer_weights(dims.d, dims.H, dims.Hkv, dims.hd, dims.F, seed=seed)
+    w["g_attn"] = (1.0 + synth.normal((dims.d,), 0.1, seed + 1)).to(BF16)
+    w["g_ffn"] = (1.0 + synth.normal((dims.d,), 0.1, seed + 2)).to(BF16)
+    return w
 
-    dims, L, skip, k = W.LLADA_STEP, 32, W.STEP_SKIP, W.STEP_TOPK
-    B, S, d, H, Hkv, hd, V = dims.B, dims.S, dims.d, dims.H, dims.Hkv, dims.hd, dims.V
-    scale = 1.0 / math.sqrt(hd)
-    print(f"full-shape batched step: {dims}, {L} layers", flush=True)
-    w = synth.layer_weights(d, H, Hkv, hd, dims.F, seed=9100)
-    w["g_attn"] = (1.0 + synth.normal((d,), 0.1, 9101)).to(BF16)
-    w["g_ffn"] = (1.0 + synth.normal((d,), 0.1, 9102)).to(BF16)
-    wbits = {n: bits(t) for n, t in w.items()}
+
+def make_model(lib, dims, L, skip, k, alpha, m_cap, w):
+    from token_skipping_partial_amd.step import EarlySkipModel, LayerWeights, SelectConfig
     lw = LayerWeights.from_dict({n: t.cuda() for n, t in w.items()})
-    shape = lib.Shape(B=B, S=S, d=d, H=H, Hkv=Hkv, hd=hd, F=dims.F, dtype="bf16", V=V)
-    model = EarlySkipModel(shape, [lw] * L, skip, SelectConfig(mode=lib.SEL_TOPK, k=k, alpha=0.5),
-                           m_cap=B * k)
+    shape = lib.Shape(B=dims.B, S=dims.S, d=dims.d, H=dims.H, Hkv=dims.Hkv, hd=dims.hd, F=dims.F,
+                      dtype="bf16", V=dims.V)
+    return EarlySkipModel(shape, [lw] * L, skip, SelectConfig(mode=lib.SEL_TOPK, k=k, alpha=alpha),
+                          m_cap=m_cap)
+
+
+def check_step(model, dims, wbits, tag, seqs, k, h_prev, logits, alpha, force, rng):
+    """Selection of `seqs` from the library's stored inputs, then sampled rows of every layer."""
+    B, S, H, Hkv, hd = dims.B, dims.S, dims.H, dims.Hkv, dims.hd
+    L, skip = len(model.layers), model.skip
+    rp = model.step1.row_ptr.cpu().numpy()
+    sel_gpu = model.step1.sel_idx.cpu().numpy()[: rp[-1]]
+    rows_of = {}
+    for b in seqs:
+        score, _, _ = O.saliency(bits(model.hidden[skip][b:b + 1]), bits(h_prev[b:b + 1]),
+                                 None if logits is None else bits(logits[b:b + 1]), alpha)
+        fl = None if force is None else force[b:b + 1]
+        cand = score if fl is None else score[fl == 0].reshape(1, -1)
+        margin = topk_margin(cand, k)
+        print(f"{tag} sequence {b}: oracle score margin {margin:.3e}", flush=True)
+        assert margin >= 1e-4, "inputs too close to the selection boundary"
+        osel, orp = O.select_compact(score, fl, O.SEL_TOPK, k=k)
+        mine = sel_gpu[rp[b]:rp[b + 1]] - b * S
+        assert np.array_equal(mine, osel[: orp[-1]]), f"{tag} sequence {b} selection"
+        rows_of[b] = mine
+    idx = torch.tensor(seqs, device="cuda")
+    scale = 1.0 / math.sqrt(hd)
+    for l in range(L):
+        picks = []
+        for b in seqs:
+            pool = np.arange(S) if l < skip else rows_of[b]
+            picks.append(np.sort(rng.choice(pool, PER_SEQ, replace=False)).astype(np.int32))
+        sel = np.concatenate([i * S + p for i, p in enumerate(picks)]).astype(np.int32)
+        srp = np.arange(0, PER_SEQ * (len(seqs) + 1), PER_SEQ, dtype=np.int32)
+        _, _, k2, v2, y2 = O.selected_layer(
+            bits(model.hidden[l][idx]), wbits, sel, srp, bits(model.k[l][idx]),
+            bits(model.v[l][idx]), bits(model.hidden[l + 1][idx]), H, Hkv, hd, EPS, scale,
+            store="bf16")
+        kg, vg, yg = host(model.k[l][idx]), host(model.v[l][idx]), host(model.hidden[l + 1][idx])
+        for i, p in enumerate(picks):
+            where = f"{tag} layer {l} sequence {seqs[i]}"
+            assert_close(kg[i][:, p], k2[i][:, p], TOL[BF16], f"{where} K rows")
+            assert_close(vg[i][:, p], v2[i][:, p], TOL[BF16], f"{where} V rows")
+            assert_close(yg[i][p], y2[i][p], TOL[BF16], f"{where} hidden rows")
+    print(f"{tag}: selection and {L} layers checked", flush=True)
+
+
+def test_llada_step_full_shape_teacher_forced(lib):
+    """The batched LLaDA-8B step (the default bench line): 32 layers, B = 8, alpha 0.5 with the
+    full vocabulary, top-205, sequences 0 and 5 checked."""
+    dims, L, skip, k = W.LLADA_STEP, 32, W.STEP_SKIP, W.STEP_TOPK
+    B, S, d, V = dims.B, dims.S, dims.d, dims.V
+    print(f"full-shape batched step: {dims}, {L} layers", flush=True)
+    w = shared_weights(dims, 9100)
+    wbits = {n: bits(t) for n, t in w.items()}
+    model = make_model(lib, dims, L, skip, k, 0.5, B * k, w)
     x = synth.normal((B, S, d), 1.0, 9200, BF16, "cuda")
     model.fill(x)
-    idx = torch.tensor(SEQS, device="cuda")
     rng = np.random.default_rng(9700)
     for t in range(2):
         large = synth.large_positions(B, S, W.LLADA_LARGE, seed=9300 + t)
@@ -81,36 +135,57 @@ def test_llada_step_full_shape_teacher_forced(lib):
         h_prev = model.h_ref.clone()
         model.step(x, logits)
         torch.cuda.synchronize()
-        print(f"step {t}: checking the selection", flush=True)
-        rp = model.step1.row_ptr.cpu().numpy()
-        assert rp[-1] == B * k
-        sel_gpu = model.step1.sel_idx.cpu().numpy()[: rp[-1]]
-        rows_of = {}
-        for b in SEQS:
-            score, _, _ = O.saliency(bits(model.hidden[skip][b:b + 1]), bits(h_prev[b:b + 1]),
-                                     bits(logits[b:b + 1]), 0.5)
-            assert topk_margin(score, k) >= 1e-4, "inputs too close to the selection boundary"
-            osel, orp = O.select_compact(score, None, O.SEL_TOPK, k=k)
-            mine = sel_gpu[rp[b]:rp[b + 1]] - b * S
-            assert np.array_equal(mine, osel[: orp[-1]]), f"step {t} sequence {b} selection"
-            rows_of[b] = mine
+        assert int(model.step1.row_ptr[-1]) == B * k
+        check_step(model, dims, wbits, f"step {t}", SEQS, k, h_prev, logits, 0.5, None, rng)
         del logits
-        for l in range(L):
-            # rows to check: any positions in the dense layers, selected ones above
-            picks = []
-            for b in SEQS:
-                pool = np.arange(S) if l < skip else rows_of[b]
-                picks.append(np.sort(rng.choice(pool, PER_SEQ, replace=False)).astype(np.int32))
-            sel = np.concatenate([i * S + p for i, p in enumerate(picks)]).astype(np.int32)
-            srp = np.array([0, PER_SEQ, 2 * PER_SEQ], np.int32)
-            _, _, k2, v2, y2 = O.selected_layer(
-                bits(model.hidden[l][idx]), wbits, sel, srp, bits(model.k[l][idx]),
-                bits(model.v[l][idx]), bits(model.hidden[l + 1][idx]), H, Hkv, hd, EPS, scale,
-                store="bf16")
-            kg, vg, yg = host(model.k[l][idx]), host(model.v[l][idx]), host(model.hidden[l + 1][idx])
-            for i, p in enumerate(picks):
-                tag = f"step {t} layer {l} sequence {SEQS[i]}"
-                assert_close(kg[i][:, p], k2[i][:, p], TOL[BF16], f"{tag} K rows")
-                assert_close(vg[i][:, p], v2[i][:, p], TOL[BF16], f"{tag} V rows")
-                assert_close(yg[i][p], y2[i][p], TOL[BF16], f"{tag} hidden rows")
-        print(f"step {t}: {L} layers checked", flush=True)
+
+
+@pytest.mark.parametrize("frac", [0.10, 0.25])
+def test_dream_step_full_shape_teacher_forced(lib, frac):
+    """The Dream-7B GQA step: 28 layers, d = 3584, 28 query heads on 4 kv heads of 128, FFN
+    18944, B = 16, S = 2048, alpha 0 (change only), exactly k tokens moved per sequence and
+    step, top-k at 10% and 25%; sequences 3 and 12 checked."""
+    dims, L, skip = W.DREAM_GQA, 28, 4
+    B, S, d = dims.B, dims.S, dims.d
+    k = round(frac * S)
+    print(f"full-shape Dream step at {frac:.0%} (k = {k}): {dims}", flush=True)
+    w = shared_weights(dims, 9800)
+    wbits = {n: bits(t) for n, t in w.items()}
+    model = make_model(lib, dims, L, skip, k, 0.0, B * k, w)
+    x = synth.normal((B, S, d), 1.0, 9810, BF16, "cuda")
+    model.fill(x)
+    rng = np.random.default_rng(9820)
+    for t in range(2):
+        large = synth.large_positions(B, S, k, seed=9830 + t)
+        x = synth.perturb(x, large.cuda(), seed=9840 + t)
+        h_prev = model.h_ref.clone()
+        model.step(x)
+        torch.cuda.synchronize()
+        check_step(model, dims, wbits, f"step {t}", (3, 12), k, h_prev, None, 0.0, None, rng)
+
+
+def test_long_context_step_full_shape_teacher_forced(lib):
+    """Long-context block decoding: 32 LLaDA-8B layers, B = 1, S = 4096 (3584 prompt + 16 blocks
+    of 32), alpha 0, the active block forced plus the top-64 by change among the other positions
+    (SlowFast, German summary page, "Der SlowFast-Algorithmus" item 2); the block advances by
+    one between the two steps."""
+    dims, L, skip, k, P, BL = W.LLADA_LONG, 32, 4, 64, 3584, 32
+    S, d = dims.S, dims.d
+    print(f"full-shape long-context step: {dims}, {L} layers", flush=True)
+    w = shared_weights(dims, 9900)
+    wbits = {n: bits(t) for n, t in w.items()}
+    model = make_model(lib, dims, L, skip, k, 0.0, k + BL, w)
+    x = synth.normal((1, S, d), 1.0, 9910, BF16, "cuda")
+    model.fill(x)
+    rng = np.random.default_rng(9920)
+    for t in range(2):
+        flags = np.zeros((1, S), np.uint8)
+        flags[0, P + t * BL:P + (t + 1) * BL] = 1
+        block = torch.from_numpy(flags.astype(bool))
+        large = synth.large_positions(1, S, k, seed=9930 + t, exclude=block) | block
+        x = synth.perturb(x, large.cuda(), seed=9940 + t)
+        h_prev = model.h_ref.clone()
+        model.step(x, force=torch.from_numpy(flags).cuda())
+        torch.cuda.synchronize()
+        assert int(model.step1.row_ptr[-1]) == k + BL
+        check_step(model, dims, wbits, f"step {t}", (0,), k, h_prev, None, 0.0, flags, rng)
