@@ -54,6 +54,7 @@ struct AttnArgs {
   const uint16_t* k_old;  // [m_cap, Hkv, hd]
   const uint16_t* v_old;
   int q_first;            // stable-token pass: positions q_first .. S-1 of every sequence
+  int qtiles;             // > 0: 1-D grid of groups x qtiles query tiles, XCD-grouped (FULL only)
 };
 constexpr int kDeltaMaxS = kSalientMaxS;  // the changed-position list of a sequence lives in LDS
 
@@ -210,9 +211,12 @@ struct VtFrag<64> {
 // epilogue adds it to the stored state. Rows of selected positions are computed too and are
 // overwritten by the exact pass that runs next.
 //
-// FULL: launch-class tag, true when the call has room for every position of every sequence as a
-// query row (m_cap >= B S: the dense layers). The code is the same; the separate instantiation
-// lets kernel traces tell the dense and the selected-row launches apart.
+// FULL: the call has room for every position of every sequence as a query row (m_cap >= B S: the
+// dense layers), so every query tile of a (sequence, kv head) has rows. With a.qtiles > 0 the
+// grid is 1-D and the query tiles of one K/V panel are dispatched together on one XCD: workgroup
+// ids x, x+8, x+16, ... share an L2, and the panel's a.qtiles tiles take consecutive ones of
+// them, so the panel is fetched from HBM once rather than once per round of workgroups. (The
+// selected-row launches keep the 2-D grid: there most tiles past the first are empty.)
 template <int HD, int NW, int ST, bool DELTA, bool FULL = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(AttnArgs a) {
@@ -232,14 +236,22 @@ void attn_bf16_kernel(AttnArgs a) {
   const int G = a.H / a.Hkv;
   const int Nq = a.H * HD;
   const int per_b = a.Hkv * a.nsplit;
-  const int b = blockIdx.x / per_b;
-  const int hk = (blockIdx.x - b * per_b) / a.nsplit;
-  const int split = blockIdx.x - b * per_b - hk * a.nsplit;
+  int bx = blockIdx.x, by = blockIdx.y;
+  if constexpr (FULL) {
+    if (a.qtiles > 0) {  // id l on XCD l % 8; that XCD's (l / 8)-th workgroup
+      const int slot = (int)blockIdx.x >> 3;
+      by = slot % a.qtiles;
+      bx = (slot / a.qtiles) * 8 + ((int)blockIdx.x & 7);
+    }
+  }
+  const int b = bx / per_b;
+  const int hk = (bx - b * per_b) / a.nsplit;
+  const int split = bx - b * per_b - hk * a.nsplit;
   const int M = min(a.row_ptr[a.B], a.m_cap);
   const int r0 = min(a.row_ptr[b], M), r1 = min(a.row_ptr[b + 1], M);
   const int nA = r1 - r0;  // selected (changed) positions of the sequence
   const int nrows = DELTA ? (a.S - a.q_first) * G : nA * G;
-  const int tile0 = blockIdx.y * TQ;
+  const int tile0 = by * TQ;
   if (tile0 >= nrows) return;
   // key range [t0, t1) of this split; DELTA: entries [0, nA) of the changed list, 32 per tile
   const int t0 = DELTA ? 0 : split * a.kps;
@@ -834,8 +846,14 @@ static hipError_t launch_exact_bf16(const ProjShape& s, float scale, const void*
   }
   const int G = s.H / s.Hkv;
   const int rows_max = (s.m_cap < s.S ? s.m_cap : s.S) * G;
-  dim3 grid(s.B * s.Hkv * a.nsplit, cdiv(rows_max, 32 * c.nw));
+  const int groups = s.B * s.Hkv * a.nsplit, qtiles = cdiv(rows_max, 32 * c.nw);
+  dim3 grid(groups, qtiles);
   const bool full = (long)s.m_cap >= (long)s.B * s.S;
+  a.qtiles = 0;
+  if (full && groups % 8 == 0 && qtiles > 1) {
+    a.qtiles = qtiles;
+    grid = dim3((unsigned)(groups * qtiles));
+  }
   if (s.hd == 64)
     full ? launch_bf16<64, true>(c, grid, a, st) : launch_bf16<64, false>(c, grid, a, st);
   else
