@@ -607,6 +607,111 @@ __device__ __forceinline__ bf16x8 frag32(const char* slot, int row, int chunk) {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Tile of this workgroup (32 x 32 x 16 kernels). Workgroups are dispatched to the 8 XCDs
+// round-robin by linear id, so ids x, x+8, x+16, ... share one L2. They are given one contiguous
+// run of the tile sequence, which walks g.group M-tiles at a time across all N-tiles: the tiles
+// resident on an XCD together then share few X and W panels.
+__device__ __forceinline__ void tile_order(const GemmArgs& g, int& mt, int& nt) {
+  const int NT = gridDim.x, MT = gridDim.y, T = NT * MT;
+  const int lin = blockIdx.x + blockIdx.y * NT;
+  const int tt = (T % 8 == 0) ? (lin % 8) * (T / 8) + lin / 8 : lin;
+  const int gm = g.group * NT;
+  const int first = (tt / gm) * g.group;
+  const int gsize = min(MT - first, g.group);
+  mt = first + (tt % gm) % gsize;
+  nt = (tt % gm) / gsize;
+}
+
+// Epilogue of a 32 x 32 x 16 tile: the wave's accumulators (MB x NB blocks of 32 x 32) go through
+// `epi` (or, for a K split, into the float32 partials of split `split`).
+template <int BM, int BN, int WM, int WN, bool SWIGLU, class Epi, int MB, int NB>
+__device__ __forceinline__ void epilogue32(const GemmArgs& g, const Epi& epi, f32x16 (&acc)[MB][NB],
+                                           int m0, int n0, int M, int wm, int wn, int l32, int h,
+                                           int split) {
+  constexpr int WTM = BM / WM;
+  // acc[i][j][4 q + r] = C[m = m0 + wm WTM + 32 i + l32][n = n0 + (n-block j) + 8 q + 4 h + r]
+  // Per 32-row block: every load the epilogue needs is issued first (rows past M load row M-1,
+  // columns past N column 0), then the stores, masked to the rows below M (and, when the tile
+  // reaches past N, to the columns below it). The branches are uniform and sit outside the
+  // store sequences, so each store waits only for its own loads (on gfx9 stores count against
+  // the same counter as loads: a wait placed at a branch join would wait for every earlier
+  // store too).
+  constexpr int NJ = SWIGLU ? NB / 2 : NB;
+  const bool cols_in = n0 + (SWIGLU ? BN / 2 : BN) <= g.N;
+  auto col = [&](int q, int j) __attribute__((always_inline)) {
+    return n0 + wrow32<BN, WN, NB, SWIGLU>(wn, j) + 8 * q + 4 * h;
+  };
+  auto gate = [&](int i, int j, int q, float (&v)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+  };
+  if (g.partial) {  // K-split partials: [split][row][N] ([split][row][gate 0..N | up N..2N])
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int m = m0 + wm * WTM + 32 * i + l32;
+      if (m >= M) continue;
+      float* pr = g.partial + ((size_t)split * g.m_cap + m) * ((SWIGLU ? 2 : 1) * (size_t)g.N);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int n = col(q, j);
+          if (!cols_in && n >= g.N) continue;
+          float v[4];
+          gate(i, j, q, v);
+          Elem<float>::store4(pr + n, v);
+          if constexpr (SWIGLU) {
+            gate(i, j + NB / 2, q, v);
+            Elem<float>::store4(pr + g.N + n, v);
+          }
+        }
+    }
+    return;
+  }
+  // the rows' addresses (which may load an index) for every block before the first store
+  decltype(epi.row(0)) ers[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) ers[i] = epi.row(min(m0 + wm * WTM + 32 * i + l32, M - 1));
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + wm * WTM + 32 * i + l32;
+    const auto& er = ers[i];
+    typename Epi::Pre pre[4][NJ];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int n = col(q, j);
+        pre[q][j] = epi.pre(er, (cols_in || n < g.N) ? n : 0);
+      }
+    if (m >= M) continue;
+    auto store = [&](int q, int j) __attribute__((always_inline)) {
+      const int n = col(q, j);
+      float v[4];
+      gate(i, j, q, v);
+      if constexpr (SWIGLU) {
+        float u[4];
+        gate(i, j + NB / 2, q, u);
+        epi(er, n, v, u, pre[q][j]);
+      } else {
+        epi(er, n, v, pre[q][j]);
+      }
+    };
+    if (cols_in) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) store(q, j);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          if (col(q, j) < g.N) store(q, j);
+    }
+  }
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int ST, bool SWIGLU, class Epi>
 __global__ __launch_bounds__(64 * WM * WN) void gemm32_bf16_kernel(GemmArgs g, Epi epi) {
   constexpr int NW = WM * WN;
@@ -619,21 +724,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_bf16_kernel(GemmArgs g, E
   __shared__ __attribute__((aligned(1024))) char ring[ST * SLOT];
 
   const int M = live_rows(g.row_ptr, g.B, g.m_cap);
-  // Tile order: workgroups are dispatched to the 8 XCDs round-robin by linear id, so ids
-  // x, x+8, x+16, ... share one L2. They are given one contiguous run of the tile sequence, which
-  // walks g.group M-tiles at a time across all N-tiles: the tiles resident on an XCD together then
-  // share few X and W panels.
-  int mt = blockIdx.y, nt = blockIdx.x;
-  {
-    const int NT = gridDim.x, MT = gridDim.y, T = NT * MT;
-    const int lin = blockIdx.x + blockIdx.y * NT;
-    const int tt = (T % 8 == 0) ? (lin % 8) * (T / 8) + lin / 8 : lin;
-    const int gm = g.group * NT;
-    const int first = (tt / gm) * g.group;
-    const int gsize = min(MT - first, g.group);
-    mt = first + (tt % gm) % gsize;
-    nt = (tt % gm) / gsize;
-  }
+  int mt, nt;
+  tile_order(g, mt, nt);
   const int m0 = mt * BM;
   if (m0 >= M) return;
   const int n0 = nt * (SWIGLU ? BN / 2 : BN);
@@ -767,87 +859,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_bf16_kernel(GemmArgs g, E
 
   }
 #undef ISSUE32
-  // acc[i][j][4 q + r] = C[m = m0 + wm WTM + 32 i + l32][n = n0 + (n-block j) + 8 q + 4 h + r]
-  // Per 32-row block: every load the epilogue needs is issued first (rows past M load row M-1,
-  // columns past N column 0), then the stores, masked to the rows below M (and, when the tile
-  // reaches past N, to the columns below it). The branches are uniform and sit outside the
-  // store sequences, so each store waits only for its own loads (on gfx9 stores count against
-  // the same counter as loads: a wait placed at a branch join would wait for every earlier
-  // store too).
-  constexpr int NJ = SWIGLU ? NB / 2 : NB;
-  const bool cols_in = n0 + (SWIGLU ? BN / 2 : BN) <= g.N;
-  auto col = [&](int q, int j) __attribute__((always_inline)) {
-    return n0 + wrow32<BN, WN, NB, SWIGLU>(wn, j) + 8 * q + 4 * h;
-  };
-  auto gate = [&](int i, int j, int q, float (&v)[4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
-  };
-  if (g.partial) {  // K-split partials: [split][row][N] ([split][row][gate 0..N | up N..2N])
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int m = m0 + wm * WTM + 32 * i + l32;
-      if (m >= M) continue;
-      float* pr = g.partial + ((size_t)blockIdx.z * g.m_cap + m) * ((SWIGLU ? 2 : 1) * (size_t)g.N);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int n = col(q, j);
-          if (!cols_in && n >= g.N) continue;
-          float v[4];
-          gate(i, j, q, v);
-          Elem<float>::store4(pr + n, v);
-          if constexpr (SWIGLU) {
-            gate(i, j + NB / 2, q, v);
-            Elem<float>::store4(pr + g.N + n, v);
-          }
-        }
-    }
-    return;
-  }
-  // the rows' addresses (which may load an index) for every block before the first store
-  decltype(epi.row(0)) ers[MB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i) ers[i] = epi.row(min(m0 + wm * WTM + 32 * i + l32, M - 1));
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int m = m0 + wm * WTM + 32 * i + l32;
-    const auto& er = ers[i];
-    typename Epi::Pre pre[4][NJ];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int n = col(q, j);
-        pre[q][j] = epi.pre(er, (cols_in || n < g.N) ? n : 0);
-      }
-    if (m >= M) continue;
-    auto store = [&](int q, int j) __attribute__((always_inline)) {
-      const int n = col(q, j);
-      float v[4];
-      gate(i, j, q, v);
-      if constexpr (SWIGLU) {
-        float u[4];
-        gate(i, j + NB / 2, q, u);
-        epi(er, n, v, u, pre[q][j]);
-      } else {
-        epi(er, n, v, pre[q][j]);
-      }
-    };
-    if (cols_in) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) store(q, j);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          if (col(q, j) < g.N) store(q, j);
-    }
-  }
+  epilogue32<BM, BN, WM, WN, SWIGLU>(g, epi, acc, m0, n0, M, wm, wn, l32, h, blockIdx.z);
 }
 
 // fixed-order sum of the K-split gate and up partials, then SiLU(gate) * up
