@@ -56,6 +56,9 @@ struct GemmPlan {
   int st;      // ring slots
   int splits;  // K partitions reduced in a second pass (1 = fused epilogue)
   int mfma = 16;  // matrix-core block edge: 16 (16x16x32) or 32 (32x32x16)
+  // > 0 (32 x 32 x 16, one K partition): rows [0, rows_big) on 256-row tiles and the rest on
+  // 128-row tiles, two launches; bm / bn / ... then describe the 256-row part
+  int rows_big = 0;
 };
 // N = output columns (SwiGLU: F, the tile then holds gate and up rows of the same columns)
 GemmPlan plan_gemm(bool bf16, int rows, int N, int K, bool swiglu);
