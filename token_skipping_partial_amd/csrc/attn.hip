@@ -211,12 +211,14 @@ struct VtFrag<64> {
 // epilogue adds it to the stored state. Rows of selected positions are computed too and are
 // overwritten by the exact pass that runs next.
 //
-// FULL: the call has room for every position of every sequence as a query row (m_cap >= B S: the
-// dense layers), so every query tile of a (sequence, kv head) has rows. With a.qtiles > 0 the
+// FULL: the call is planned for every position of every sequence as a query row (m_plan >= B S:
+// the dense layers), so every query tile of a (sequence, kv head) has rows. With a.qtiles > 0 the
 // grid is 1-D and the query tiles of one K/V panel are dispatched together on one XCD: workgroup
 // ids x, x+8, x+16, ... share an L2, and the panel's a.qtiles tiles take consecutive ones of
 // them, so the panel is fetched from HBM once rather than once per round of workgroups. (The
-// selected-row launches keep the 2-D grid: there most tiles past the first are empty.)
+// selected-row launches keep the 2-D grid: there most tiles past the first are empty. A call with
+// room for every position but planned for fewer rows, as in the layer-adaptive step, is one of
+// them: on the 1-D grid its few live tiles sat behind empty ones, 9.0 vs 8.5 ms per 32-layer step.)
 template <int HD, int NW, int ST, bool DELTA, bool FULL = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(AttnArgs a) {
@@ -848,7 +850,7 @@ static hipError_t launch_exact_bf16(const ProjShape& s, float scale, const void*
   const int rows_max = (s.m_cap < s.S ? s.m_cap : s.S) * G;
   const int groups = s.B * s.Hkv * a.nsplit, qtiles = cdiv(rows_max, 32 * c.nw);
   dim3 grid(groups, qtiles);
-  const bool full = (long)s.m_cap >= (long)s.B * s.S;
+  const bool full = (long)s.m_plan >= (long)s.B * s.S;
   a.qtiles = 0;
   if (full && groups % 8 == 0 && qtiles > 1) {
     a.qtiles = qtiles;
