@@ -9,6 +9,8 @@ at early layers such as 1/8 of the depth; the selection is reused by the layers 
 A layer-adaptive step (DyLLM, French summary page §2.A and §2.B) keeps the attention context of
 every token in every layer and lets each layer pick, by the cosine change of the contexts, the
 tokens whose FFN is recomputed; those tokens' changed outputs decide the next layer's rows.
+Every driver can write its carried state to a file and resume from it (`save_state`,
+`load_state`).
 """
 from __future__ import annotations
 
@@ -138,6 +140,64 @@ class SingleLayerStep:
                        self.scratch, stream)
 
 
+# ---------------------------------------------------------------- checkpoint / resume
+# A step driver's state is what its next step reads from the steps before it: the K/V and hidden
+# caches, the skip-layer references, and for the layer-adaptive driver the attention states,
+# contexts and launch plans. `state_dict` copies it to host memory (after the device has
+# finished), `load_state_dict` copies it back into the driver's own buffers in place, so HIP
+# graphs captured on the driver stay valid. A resumed driver's next step is bit-identical to the
+# uninterrupted one's. Files hold plain tensors, numbers and strings (`torch.load(...,
+# weights_only=True)` reads them).
+STATE_FORMAT = "dllm-step-state/1"
+
+
+def _shape_key(shape: Shape) -> list:
+    return [shape.B, shape.S, shape.d, shape.H, shape.Hkv, shape.hd, shape.F, shape.V,
+            "bf16" if shape.torch_dtype == torch.bfloat16 else "f32"]
+
+
+def _snapshot(config: dict, tensors: dict, scalars: dict) -> dict:
+    if any(t.is_cuda for t in tensors.values()):
+        torch.cuda.synchronize()
+    return {"format": STATE_FORMAT, "config": dict(config),
+            "tensors": {n: t.detach().to("cpu", copy=True) for n, t in tensors.items()},
+            "scalars": dict(scalars)}
+
+
+def _restore(state: dict, config: dict, tensors: dict) -> dict:
+    """Checks the state against the driver's configuration and buffers, copies the tensors in
+    place and returns the scalars."""
+    if not isinstance(state, dict) or state.get("format") != STATE_FORMAT:
+        raise ValueError(f"not a {STATE_FORMAT} state")
+    got = state["config"]
+    for key in sorted(set(config) | set(got)):
+        if got.get(key) != config.get(key):
+            raise ValueError(f"state was saved with {key} = {got.get(key)!r}, this driver has "
+                             f"{config.get(key)!r}")
+    saved = state["tensors"]
+    if set(saved) != set(tensors):
+        raise ValueError(f"state tensors {sorted(set(saved) ^ set(tensors))} do not match")
+    for n, t in tensors.items():
+        if saved[n].shape != t.shape or saved[n].dtype != t.dtype:
+            raise ValueError(f"state tensor {n}: {tuple(saved[n].shape)} {saved[n].dtype}, "
+                             f"buffer {tuple(t.shape)} {t.dtype}")
+    for n, t in tensors.items():
+        t.copy_(saved[n])
+    if any(t.is_cuda for t in tensors.values()):
+        torch.cuda.synchronize()
+    return dict(state["scalars"])
+
+
+def save_state(driver, path) -> None:
+    """Writes `driver.state_dict()` to `path`."""
+    torch.save(driver.state_dict(), path)
+
+
+def load_state(driver, path) -> None:
+    """Restores a state written by `save_state` into `driver` (same configuration and shapes)."""
+    driver.load_state_dict(torch.load(path, map_location="cpu", weights_only=True))
+
+
 class EarlySkipModel:
     """L-layer early-skip step with per-layer K/V caches and per-boundary hidden-state caches.
 
@@ -225,6 +285,30 @@ class EarlySkipModel:
                            self.hidden[l + 1], s2.sel_idx, s2.row_ptr, s2.scratch, stream,
                            mark, "sel2_")
         return s2.sel_idx, s2.row_ptr
+
+
+    def _carried(self) -> dict:
+        t = {}
+        for l in range(len(self.layers)):
+            t[f"k.{l}"], t[f"v.{l}"] = self.k[l], self.v[l]
+        for l, h in enumerate(self.hidden):
+            t[f"hidden.{l}"] = h
+        t["h_ref"] = self.h_ref
+        if self.skip2:
+            t["h_ref2"] = self.h_ref2
+        return t
+
+    def _config(self) -> dict:
+        return {"driver": "EarlySkipModel", "shape": _shape_key(self.shape),
+                "layers": len(self.layers), "skip": self.skip, "skip2": self.skip2,
+                "k2": self.k2, "m_cap": self.m_cap}
+
+    def state_dict(self) -> dict:
+        """K/V caches, hidden-state caches and skip-layer references, copied to the host."""
+        return _snapshot(self._config(), self._carried(), {})
+
+    def load_state_dict(self, state: dict) -> None:
+        _restore(state, self._config(), self._carried())
 
 
 class LayerAdaptiveModel:
@@ -390,6 +474,45 @@ class LayerAdaptiveModel:
         return self.sel, self.rp
 
 
+    def _settle_counts(self) -> None:
+        """Waits for the row counts in flight and folds them into the plans, as the next step
+        would once they have arrived (so that step's plans no longer depend on timing)."""
+        if self._counts_evt is not None:
+            self._counts_evt.synchronize()
+            self._plans[self._counts_kind] = [c + c // 8 + 1 for c in self._counts_host.tolist()]
+            self._counts_evt = None
+
+    def _carried(self) -> dict:
+        t = {"x_ref": self.x_ref}
+        for l in range(len(self.layers)):
+            t[f"k.{l}"], t[f"v.{l}"], t[f"q_all.{l}"] = self.k[l], self.v[l], self.q_all[l]
+            t[f"st_m.{l}"], t[f"st_l.{l}"], t[f"st_o.{l}"] = self.st_m[l], self.st_l[l], self.st_o[l]
+            t[f"ctx.{l}.0"], t[f"ctx.{l}.1"] = self.ctx[l]
+        for l, h in enumerate(self.hidden):
+            t[f"hidden.{l}"] = h
+        return t
+
+    def _config(self) -> dict:
+        return {"driver": "LayerAdaptiveModel", "shape": _shape_key(self.shape),
+                "layers": len(self.layers), "prompt_len": self.prompt_len,
+                "inject_every": self.inject_every}
+
+    def state_dict(self) -> dict:
+        """Caches, attention states and contexts, the step counter, the index of the current
+        context buffer and the launch plans (row counts still in flight are waited for)."""
+        self._settle_counts()
+        plans = {("inject" if k else "response"): list(v) for k, v in self._plans.items()}
+        return _snapshot(self._config(), self._carried(),
+                         {"t": self.t, "cur": self.cur, "plans": plans})
+
+    def load_state_dict(self, state: dict) -> None:
+        sc = _restore(state, self._config(), self._carried())
+        self.t, self.cur = int(sc["t"]), int(sc["cur"])
+        self._plans = {k == "inject": [int(c) for c in v] for k, v in sc["plans"].items()}
+        self._counts_evt = None
+        self.plan = [0] * len(self.plan)
+
+
 class BlockDecoder:
     """Semi-autoregressive block decoding that stays on the device: the early-skip step
     (ES-dLLM, German summary page §2.B) with the active block forced into the selection, then the
@@ -462,3 +585,21 @@ class BlockDecoder:
                 self.step(logits)
         torch.cuda.current_stream().wait_stream(side)
         return g
+
+    def _config(self) -> dict:
+        return {"driver": "BlockDecoder", "prompt_len": self.P, "block_len": self.L,
+                "tau": float(self.tau), "k_min": self.k_min}
+
+    def _carried(self) -> dict:
+        return {"tok": self.tok, "blk": self.blk, "flags": self.flags, "x": self.x}
+
+    def state_dict(self) -> dict:
+        """Token ids, block indices, selection flags and the next step's input rows, with the
+        model's state under "model"."""
+        st = _snapshot(self._config(), self._carried(), {})
+        st["model"] = self.model.state_dict()
+        return st
+
+    def load_state_dict(self, state: dict) -> None:
+        _restore(state, self._config(), self._carried())
+        self.model.load_state_dict(state["model"])
