@@ -57,6 +57,8 @@
  *     deltas are float32; indices are int32; the force mask is uint8.
  *   - bf16 tensors are multiplied on the matrix cores with float32 accumulation; norms, softmax
  *     and SwiGLU are evaluated in float32.
+ *   - Each call is one roctx range named after the call (host part: checks and enqueues), seen
+ *     by `rocprofv3 --marker-trace`; the library links librocprofiler-sdk-roctx for it.
  */
 #ifndef DLLM_H_
 #define DLLM_H_

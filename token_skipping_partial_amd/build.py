@@ -37,6 +37,7 @@ def command(out: str = LIB) -> list:
         "-Wall", "-Wno-unused-result",
         "-I", os.path.join(ROOT, "include"),
         *[os.path.join(CSRC, s) for s in SOURCES],
+        "-L", "/opt/rocm/lib", "-lrocprofiler-sdk-roctx",
         "-o", out,
     ]
 

@@ -5,6 +5,8 @@
 
 #include <mutex>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "dllm.h"
 #include "kernels.h"
 
@@ -38,6 +40,16 @@ ProjShape proj_shape(const dllm_shape* s, int32_t m_cap) {
   p.m_plan = (s->m_plan > 0 && s->m_plan < m_cap) ? s->m_plan : m_cap;
   return p;
 }
+
+// One named roctx range per library call (its host part: checks and enqueues; the kernels it
+// launched run on the device afterwards). Shown by `rocprofv3 --marker-trace`; without a tool
+// attached a push / pop is a call into an empty table slot.
+struct CallRange {
+  explicit CallRange(const char* name) { roctxRangePushA(name); }
+  ~CallRange() { roctxRangePop(); }
+  CallRange(const CallRange&) = delete;
+  CallRange& operator=(const CallRange&) = delete;
+};
 
 dllm_status hip_status(hipError_t e) { return e == hipSuccess ? DLLM_OK : DLLM_ERR_HIP; }
 
@@ -133,6 +145,7 @@ size_t dllm_workspace_bytes(int32_t op, const dllm_shape* shape, int32_t m_cap) 
 dllm_status dllm_saliency(const dllm_shape* shape, int32_t delta_kind, float alpha,
                           const void* h_cur, const void* h_prev, const void* logits,
                           float* score, float* conf_out, float* delta_out, void* stream) {
+  CallRange range_("dllm_saliency");
   if (!base_shape_ok(shape) || !score || !(alpha >= 0.f && alpha <= 1.f) ||
       delta_kind < DLLM_DELTA_L1N || delta_kind > DLLM_DELTA_L2R)
     return DLLM_ERR_INVALID_ARG;
@@ -173,6 +186,7 @@ dllm_status dllm_saliency(const dllm_shape* shape, int32_t delta_kind, float alp
 dllm_status dllm_select_compact(const dllm_shape* shape, int32_t mode, float tau, int32_t k,
                                 const float* score, const uint8_t* force, int32_t* sel_idx,
                                 int32_t* row_ptr, void* ws, size_t ws_bytes, void* stream) {
+  CallRange range_("dllm_select_compact");
   (void)ws;
   (void)ws_bytes;
   if (!base_shape_ok(shape) || !score || !sel_idx || !row_ptr) return DLLM_ERR_INVALID_ARG;
@@ -204,6 +218,7 @@ dllm_status dllm_gather_qkv_scatter_kv(const dllm_shape* shape, const void* h_in
                                        const int32_t* sel_idx, const int32_t* row_ptr,
                                        int32_t m_cap, void* q_sel, void* k_cache, void* v_cache,
                                        void* ws, size_t ws_bytes, void* stream) {
+  CallRange range_("dllm_gather_qkv_scatter_kv");
   dllm_status st = layer_shape_status(shape, m_cap);
   if (st != DLLM_OK) return st;
   if (!h_in || !g_attn || !w_qkv || !sel_idx || !row_ptr || !q_sel || !k_cache || !v_cache)
@@ -222,6 +237,7 @@ dllm_status dllm_partial_attn(const dllm_shape* shape, float scale, const void* 
                               const void* k_cache, const void* v_cache, const int32_t* sel_idx,
                               const int32_t* row_ptr, int32_t m_cap, void* o_sel, void* ws,
                               size_t ws_bytes, void* stream) {
+  CallRange range_("dllm_partial_attn");
   dllm_status st = layer_shape_status(shape, m_cap);
   if (st != DLLM_OK) return st;
   if (!q_sel || !k_cache || !v_cache || !sel_idx || !row_ptr || !o_sel || !isfinite(scale))
@@ -241,6 +257,7 @@ dllm_status dllm_gather_ffn_scatter(const dllm_shape* shape, const void* h_in, c
                                     const int32_t* sel_idx, const int32_t* row_ptr,
                                     int32_t m_cap, void* h_out, void* ws, size_t ws_bytes,
                                     void* stream) {
+  CallRange range_("dllm_gather_ffn_scatter");
   dllm_status st = layer_shape_status(shape, m_cap);
   if (st != DLLM_OK) return st;
   if (!h_in || !o_sel || !w_o || !g_ffn || !w_gate || !w_up || !w_down || !sel_idx ||
@@ -258,6 +275,7 @@ dllm_status dllm_gather_ffn_scatter(const dllm_shape* shape, const void* h_in, c
 dllm_status dllm_gather_kv_rows(const dllm_shape* shape, const void* k_cache, const void* v_cache,
                                 const int32_t* sel_idx, const int32_t* row_ptr, int32_t m_cap,
                                 void* k_rows, void* v_rows, void* stream) {
+  CallRange range_("dllm_gather_kv_rows");
   dllm_status st = layer_shape_status(shape, m_cap);
   if (st != DLLM_OK) return st;
   if (!k_cache || !v_cache || !sel_idx || !row_ptr || !k_rows || !v_rows)
@@ -275,6 +293,7 @@ dllm_status dllm_salient_attn(const dllm_shape* shape, float scale, const void* 
                               const int32_t* row_ptr, int32_t m_cap, int32_t q_first, float* st_m,
                               float* st_l, float* st_o, void* o_sel, void* o_all, void* ws,
                               size_t ws_bytes, void* stream) {
+  CallRange range_("dllm_salient_attn");
   dllm_status st = layer_shape_status(shape, m_cap);
   if (st != DLLM_OK) return st;
   if (!q_sel || !q_all || !k_cache || !v_cache || !k_old || !v_old || !sel_idx || !row_ptr ||
@@ -295,6 +314,7 @@ dllm_status dllm_salient_attn(const dllm_shape* shape, float scale, const void* 
 dllm_status dllm_gather_rows(const dllm_shape* shape, const void* src, int32_t width,
                              const int32_t* sel_idx, const int32_t* row_ptr, int32_t m_cap,
                              void* dst, void* stream) {
+  CallRange range_("dllm_gather_rows");
   if (!base_shape_ok(shape) || width <= 0 || m_cap < 0 || (long)m_cap > (long)shape->B * shape->S)
     return DLLM_ERR_INVALID_ARG;
   if (!src || !sel_idx || !row_ptr || !dst || !aligned16(src) || !aligned16(dst))
@@ -310,6 +330,7 @@ dllm_status dllm_commit(const dllm_shape* shape, const void* logits, int32_t pro
                         int32_t block_len, float tau, int32_t k_min, int32_t* tok, int32_t* blk,
                         int32_t* committed_idx, int32_t* committed_rp, uint8_t* flags, void* ws,
                         size_t ws_bytes, void* stream) {
+  CallRange range_("dllm_commit");
   if (!base_shape_ok(shape) || !logits || !tok || !blk || !committed_idx || !committed_rp ||
       !flags || shape->V <= 0 || prompt_len < 0 || prompt_len > shape->S || block_len < 1 ||
       k_min < 0 || tau != tau || !aligned16(logits))
@@ -335,6 +356,7 @@ dllm_status dllm_commit_noalloc(const dllm_shape* shape, const void* logits, int
                                 int32_t block_len, float tau, int32_t k_min, int32_t* tok,
                                 int32_t* blk, int32_t* committed_idx, int32_t* committed_rp,
                                 uint8_t* flags, void* stream) {
+  CallRange range_("dllm_commit_noalloc");
   if (!base_shape_ok(shape) || !logits || !tok || !blk || !committed_idx || !committed_rp ||
       !flags || shape->V <= 0 || prompt_len < 0 || prompt_len > shape->S || block_len < 1 ||
       k_min < 0 || tau != tau || !aligned16(logits))
@@ -363,6 +385,7 @@ dllm_status dllm_commit_noalloc(const dllm_shape* shape, const void* logits, int
 dllm_status dllm_embed_rows(const dllm_shape* shape, const void* emb, const void* mask_emb,
                             const int32_t* tok, const int32_t* sel_idx, const int32_t* row_ptr,
                             int32_t m_cap, void* x, void* stream) {
+  CallRange range_("dllm_embed_rows");
   if (!base_shape_ok(shape) || !emb || !mask_emb || !tok || !sel_idx || !row_ptr || !x ||
       shape->V <= 0 || m_cap < 0 || (long)m_cap > (long)shape->B * shape->S)
     return DLLM_ERR_INVALID_ARG;
@@ -376,6 +399,7 @@ dllm_status dllm_embed_rows(const dllm_shape* shape, const void* emb, const void
 dllm_status dllm_flags_from_rows(const dllm_shape* shape, const uint8_t* force,
                                  const int32_t* sel_idx, const int32_t* row_ptr, int32_t m_cap,
                                  uint8_t* flags, void* stream) {
+  CallRange range_("dllm_flags_from_rows");
   if (!base_shape_ok(shape) || !sel_idx || !row_ptr || !flags || m_cap < 0 ||
       (long)m_cap > (long)shape->B * shape->S || (force && (const void*)force == (void*)flags))
     return DLLM_ERR_INVALID_ARG;
