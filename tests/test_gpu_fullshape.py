@@ -8,7 +8,9 @@ every token) and two early-skip steps with every cache carried (ES-dLLM, German 
   * the Dream-7B GQA step: 28 layers (d = 3584, 28 query heads on 4 kv heads, FFN 18944),
     B = 16, S = 2048, alpha 0, top-10% and top-25% per sequence;
   * long-context block decoding: 32 LLaDA-8B layers, B = 1, S = 4096, the active block of 32
-    forced plus the top-64 by change.
+    forced plus the top-64 by change;
+  * the layer-adaptive step (every token's context kept, per-layer FFN rows): 32 LLaDA-8B layers,
+    B = 1, S = 1024 (its own checks are listed in its docstring).
 
 After each step the oracle checks, for one or two sequences:
   * the selection: the oracle's scores from the library's own stored bf16 inputs of the skip
@@ -189,3 +191,95 @@ def test_long_context_step_full_shape_teacher_forced(lib):
         torch.cuda.synchronize()
         assert int(model.step1.row_ptr[-1]) == k + BL
         check_step(model, dims, wbits, f"step {t}", (0,), k, h_prev, None, 0.0, flags, rng)
+
+
+def test_layer_adaptive_full_shape_teacher_forced(lib):
+    """The layer-adaptive step at the LLaDA-8B shape (DyLLM, French summary page §2.A and §2.B):
+    32 layers, B = 1, S = 1024, every token's attention context kept, context thresholds at the
+    80th percentile of an untimed calibration step (as in the bench). Two steps after a fill; per
+    step the layer-0 input set against the oracle's L1-normalised change, then per layer, on 8
+    sampled rows each:
+      * input set: K/V cache rows and query cache from the library's stored input of the layer;
+      * contexts of input-set rows and of stable tokens: the exact softmax over every key of the
+        layer's cache with the token's cached query (stable tokens come from the changed-key
+        update of their stored state, carried across the steps);
+      * cosine scores of every token from the library's contexts (this and the previous step),
+        and the FFN set equal to the tokens above the layer's threshold by those scores;
+      * FFN set: output rows from the library's stored input and context; the other rows keep
+        the previous step's bits."""
+    from token_skipping_partial_amd.step import LayerAdaptiveModel, LayerWeights
+    dims, L = W.LLADA_LAYER, 32
+    B, S, d, H, Hkv, hd = dims.B, dims.S, dims.d, dims.H, dims.Hkv, dims.hd
+    nq = H * hd
+    print(f"full-shape layer-adaptive step: {dims}, {L} layers", flush=True)
+    w = shared_weights(dims, 9950)
+    wbits = {n: bits(t) for n, t in w.items()}
+    lw = LayerWeights.from_dict({n: t.cuda() for n, t in w.items()})
+    shape = lib.Shape(B=B, S=S, d=d, H=H, Hkv=Hkv, hd=hd, F=dims.F, dtype="bf16")
+    model = LayerAdaptiveModel(shape, [lw] * L, 0.05, [0.0] * L)
+    x = [synth.normal((B, S, d), 1.0, 9960, BF16, "cuda")]
+    for t in (1, 2):
+        large = synth.large_positions(B, S, W.LLADA_LARGE, seed=9970 + t)
+        x.append(synth.perturb(x[-1], large.cuda(), seed=9980 + t))
+    model.fill(x[0])
+    taus = []
+    for l in range(L):   # calibration: each layer's 80th percentile, every later layer takes all
+        model.step(x[1], tau_ctx=taus + [-1.0] * (L - l), record=True)
+        taus.append(float(torch.quantile(model.layer_scores[l].flatten(), 0.8).item()))
+        model.fill(x[0])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9990)
+    scale = 1.0 / math.sqrt(hd)
+    pick = lambda pool, n=PER_SEQ: np.sort(rng.choice(pool, min(n, len(pool)), replace=False)).astype(np.int32)  # noqa: E731
+    for t in (1, 2):
+        prev_hidden = [h.clone() for h in model.hidden]
+        x_prev = model.x_ref.clone()
+        sets, rps = model.step(x[t], tau_ctx=taus, record=True)
+        torch.cuda.synchronize()
+        score0, _, _ = O.saliency(bits(x[t]), bits(x_prev), None, 0.0, O.DELTA_L1N)
+        margin = float(np.min(np.abs(score0 - 0.05)))
+        assert margin >= 1e-4, f"step {t}: input-change margin {margin:.2e}"
+        osel, orp = O.select_compact(score0, None, O.SEL_THRESHOLD, tau=0.05)
+        n0 = int(rps[0][-1])
+        assert n0 == int(orp[-1]) and np.array_equal(sets[0][:n0].cpu().numpy(), osel[:n0]), t
+        counts = []
+        for l in range(L):
+            tag = f"step {t} layer {l}"
+            A = sets[l][:int(rps[l][-1])].cpu().numpy()
+            Fs = sets[l + 1][:int(rps[l + 1][-1])].cpu().numpy()
+            counts.append(len(Fs))
+            cur, prev = model.ctx[l][model.cur], model.ctx[l][1 - model.cur]
+            kb, vb = bits(model.k[l]), bits(model.v[l])
+            # input set: K/V and query rows from the stored layer input
+            pa = pick(A)
+            q, k2, v2 = O.gather_qkv_scatter_kv(bits(model.hidden[l]), wbits["g_attn"],
+                                                wbits["w_qkv"], pa, np.array([0, len(pa)], np.int32),
+                                                kb, vb, H, Hkv, hd, EPS, store="bf16")
+            assert_close(host(model.k[l])[0][:, pa], k2[0][:, pa], TOL[BF16], f"{tag} K rows")
+            assert_close(host(model.v[l])[0][:, pa], v2[0][:, pa], TOL[BF16], f"{tag} V rows")
+            assert_close(host(model.q_all[l])[pa], q, TOL[BF16], f"{tag} query cache rows")
+            # contexts: exact softmax over every key with the cached query
+            rows = np.sort(np.concatenate([pa, pick(np.setdiff1d(np.arange(S), A))])).astype(np.int32)
+            o = O.partial_attn(bits(model.q_all[l])[rows], kb, vb, rows,
+                               np.array([0, len(rows)], np.int32), H, Hkv, hd, scale)
+            assert_close(host(cur)[rows], o, TOL[BF16], f"{tag} contexts (input set + stable)")
+            # cosine scores from the library's contexts; the FFN set by the threshold
+            sc, _, _ = O.saliency(bits(cur).reshape(B, S, nq), bits(prev).reshape(B, S, nq), None,
+                                  0.0, O.DELTA_COS)
+            lib_sc = model.layer_scores[l].cpu().numpy()
+            err = float(np.max(np.abs(lib_sc.astype(np.float64) - sc)))
+            assert err <= 1e-4, f"{tag}: context scores differ by {err:.2e}"
+            fsel, frp = O.select_compact(lib_sc, None, O.SEL_THRESHOLD, tau=taus[l])
+            assert np.array_equal(Fs, fsel[:int(frp[-1])]), f"{tag}: FFN set"
+            # FFN rows from the stored input and context; the other rows untouched
+            pf = pick(Fs)
+            out = O.gather_ffn_scatter(bits(model.hidden[l]), bits(cur)[pf], wbits["w_o"],
+                                       wbits["g_ffn"], wbits["w_gate"], wbits["w_up"],
+                                       wbits["w_down"], pf, np.array([0, len(pf)], np.int32),
+                                       bits(model.hidden[l + 1]), EPS, store="bf16")
+            assert_close(host(model.hidden[l + 1])[0][pf], out[0][pf], TOL[BF16],
+                         f"{tag} output rows")
+            rest = pick(np.setdiff1d(np.arange(S), Fs))
+            assert np.array_equal(bits(model.hidden[l + 1])[0][rest],
+                                  bits(prev_hidden[l + 1])[0][rest]), f"{tag}: untouched rows"
+        print(f"step {t}: input rows {n0}, FFN rows per layer {counts}", flush=True)
