@@ -193,7 +193,8 @@ def test_long_context_step_full_shape_teacher_forced(lib):
         check_step(model, dims, wbits, f"step {t}", (0,), k, h_prev, None, 0.0, flags, rng)
 
 
-def test_layer_adaptive_full_shape_teacher_forced(lib):
+@pytest.mark.parametrize("P", [0, 512])
+def test_layer_adaptive_full_shape_teacher_forced(lib, P):
     """The layer-adaptive step at the LLaDA-8B shape (DyLLM, French summary page §2.A and §2.B):
     32 layers, B = 1, S = 1024, every token's attention context kept, context thresholds at the
     80th percentile of an untimed calibration step (as in the bench). Two steps after a fill; per
@@ -206,40 +207,53 @@ def test_layer_adaptive_full_shape_teacher_forced(lib):
       * cosine scores of every token from the library's contexts (this and the previous step),
         and the FFN set equal to the tokens above the layer's threshold by those scores;
       * FFN set: output rows from the library's stored input and context; the other rows keep
-        the previous step's bits."""
+        the previous step's bits.
+    P = 512 (DyLLM §2.C): positions 0-511 are a prompt, step 1 is response-only (the prompt is
+    left out of every row set and of the context update: its contexts keep their bits) and step 2
+    re-injects it (forced into every row set)."""
     from token_skipping_partial_amd.step import LayerAdaptiveModel, LayerWeights
     dims, L = W.LLADA_LAYER, 32
     B, S, d, H, Hkv, hd = dims.B, dims.S, dims.d, dims.H, dims.Hkv, dims.hd
     nq = H * hd
-    print(f"full-shape layer-adaptive step: {dims}, {L} layers", flush=True)
+    print(f"full-shape layer-adaptive step: {dims}, {L} layers, prompt {P}", flush=True)
     w = shared_weights(dims, 9950)
     wbits = {n: bits(t) for n, t in w.items()}
     lw = LayerWeights.from_dict({n: t.cuda() for n, t in w.items()})
     shape = lib.Shape(B=B, S=S, d=d, H=H, Hkv=Hkv, hd=hd, F=dims.F, dtype="bf16")
-    model = LayerAdaptiveModel(shape, [lw] * L, 0.05, [0.0] * L)
+    model = LayerAdaptiveModel(shape, [lw] * L, 0.05, [0.0] * L, prompt_len=P,
+                               inject_every=2 if P else 0)
+    prompt = torch.zeros(B, S, dtype=torch.bool)
+    prompt[:, :P] = True
     x = [synth.normal((B, S, d), 1.0, 9960, BF16, "cuda")]
     for t in (1, 2):
-        large = synth.large_positions(B, S, W.LLADA_LARGE, seed=9970 + t)
+        large = synth.large_positions(B, S, W.LLADA_LARGE, seed=9970 + t,
+                                      exclude=prompt if P else None)
         x.append(synth.perturb(x[-1], large.cuda(), seed=9980 + t))
     model.fill(x[0])
     taus = []
     for l in range(L):   # calibration: each layer's 80th percentile, every later layer takes all
         model.step(x[1], tau_ctx=taus + [-1.0] * (L - l), record=True)
-        taus.append(float(torch.quantile(model.layer_scores[l].flatten(), 0.8).item()))
+        taus.append(float(torch.quantile(model.layer_scores[l][:, P:].flatten(), 0.8).item()))
         model.fill(x[0])
     torch.cuda.synchronize()
     rng = np.random.default_rng(9990)
     scale = 1.0 / math.sqrt(hd)
     pick = lambda pool, n=PER_SEQ: np.sort(rng.choice(pool, min(n, len(pool)), replace=False)).astype(np.int32)  # noqa: E731
     for t in (1, 2):
+        inject = P > 0 and t % 2 == 0
+        flags = None
+        if P:
+            flags = np.zeros((B, S), np.uint8)
+            flags[:, :P] = 1 if inject else 2
         prev_hidden = [h.clone() for h in model.hidden]
         x_prev = model.x_ref.clone()
         sets, rps = model.step(x[t], tau_ctx=taus, record=True)
         torch.cuda.synchronize()
         score0, _, _ = O.saliency(bits(x[t]), bits(x_prev), None, 0.0, O.DELTA_L1N)
-        margin = float(np.min(np.abs(score0 - 0.05)))
+        cand0 = score0 if flags is None else score0[flags == 0]
+        margin = float(np.min(np.abs(cand0 - 0.05)))
         assert margin >= 1e-4, f"step {t}: input-change margin {margin:.2e}"
-        osel, orp = O.select_compact(score0, None, O.SEL_THRESHOLD, tau=0.05)
+        osel, orp = O.select_compact(score0, flags, O.SEL_THRESHOLD, tau=0.05)
         n0 = int(rps[0][-1])
         assert n0 == int(orp[-1]) and np.array_equal(sets[0][:n0].cpu().numpy(), osel[:n0]), t
         counts = []
@@ -258,18 +272,23 @@ def test_layer_adaptive_full_shape_teacher_forced(lib):
             assert_close(host(model.k[l])[0][:, pa], k2[0][:, pa], TOL[BF16], f"{tag} K rows")
             assert_close(host(model.v[l])[0][:, pa], v2[0][:, pa], TOL[BF16], f"{tag} V rows")
             assert_close(host(model.q_all[l])[pa], q, TOL[BF16], f"{tag} query cache rows")
-            # contexts: exact softmax over every key with the cached query
-            rows = np.sort(np.concatenate([pa, pick(np.setdiff1d(np.arange(S), A))])).astype(np.int32)
+            # contexts: exact softmax over every key with the cached query; in a response-only
+            # step the prompt's contexts keep their bits
+            lo = P if (P and not inject) else 0
+            rows = np.sort(np.concatenate([pa, pick(np.setdiff1d(np.arange(lo, S), A))])).astype(np.int32)
             o = O.partial_attn(bits(model.q_all[l])[rows], kb, vb, rows,
                                np.array([0, len(rows)], np.int32), H, Hkv, hd, scale)
             assert_close(host(cur)[rows], o, TOL[BF16], f"{tag} contexts (input set + stable)")
+            if lo:
+                pp = pick(np.arange(P))
+                assert np.array_equal(bits(cur)[pp], bits(prev)[pp]), f"{tag}: prompt contexts"
             # cosine scores from the library's contexts; the FFN set by the threshold
             sc, _, _ = O.saliency(bits(cur).reshape(B, S, nq), bits(prev).reshape(B, S, nq), None,
                                   0.0, O.DELTA_COS)
             lib_sc = model.layer_scores[l].cpu().numpy()
             err = float(np.max(np.abs(lib_sc.astype(np.float64) - sc)))
             assert err <= 1e-4, f"{tag}: context scores differ by {err:.2e}"
-            fsel, frp = O.select_compact(lib_sc, None, O.SEL_THRESHOLD, tau=taus[l])
+            fsel, frp = O.select_compact(lib_sc, flags, O.SEL_THRESHOLD, tau=taus[l])
             assert np.array_equal(Fs, fsel[:int(frp[-1])]), f"{tag}: FFN set"
             # FFN rows from the stored input and context; the other rows untouched
             pf = pick(Fs)
@@ -282,4 +301,5 @@ def test_layer_adaptive_full_shape_teacher_forced(lib):
             rest = pick(np.setdiff1d(np.arange(S), Fs))
             assert np.array_equal(bits(model.hidden[l + 1])[0][rest],
                                   bits(prev_hidden[l + 1])[0][rest]), f"{tag}: untouched rows"
-        print(f"step {t}: input rows {n0}, FFN rows per layer {counts}", flush=True)
+        print(f"step {t}{' (inject)' if inject else ''}: input rows {n0}, FFN rows per layer "
+              f"{counts}", flush=True)
