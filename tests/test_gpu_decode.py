@@ -157,7 +157,7 @@ DP, DBLK, DK, DKMIN = 16, 8, 4, 1
 EPS = 1e-5
 
 
-def decode_setup(lib, seed):
+def decode_setup(lib, seed, refresh_every=0):
     from token_skipping_partial_amd.step import (BlockDecoder, EarlySkipModel, LayerWeights,
                                                  SelectConfig)
     shape = lib.Shape(B=DB, S=DS, d=Dd, H=DH, Hkv=DHkv, hd=Dhd, F=DF, dtype="bf16", V=DV)
@@ -168,7 +168,7 @@ def decode_setup(lib, seed):
     prompt = torch.from_numpy(np.random.default_rng(seed).integers(0, DV, (DB, DP))).int().cuda()
     model = EarlySkipModel(shape, [LayerWeights.from_dict(x) for x in w], 0,
                            SelectConfig(mode=lib.SEL_TOPK, k=DK, alpha=0.0), DB * (DK + DBLK))
-    dec = BlockDecoder(model, emb, mask, DP, DBLK, TAU, DKMIN)
+    dec = BlockDecoder(model, emb, mask, DP, DBLK, TAU, DKMIN, refresh_every=refresh_every)
     dec.start(prompt)
     return dec, w, emb, mask, prompt
 
@@ -208,6 +208,12 @@ class OracleDecoder:
                                                                     DBLK, TAU, DKMIN)
         self.x = O.embed_rows(self.emb, self.mask, self.tok, c_sel, c_rp, self.x)
         return sel, rp
+
+    def refresh(self):
+        """Every layer on every token from the current input; the skip-layer reference is the
+        input itself (skip at layer 0)."""
+        self.layers(np.arange(DB * DS, dtype=np.int32), self.all_rp)
+        self.h_ref = self.x
 
 
 def test_decode_loop_matches_the_oracle(lib):
@@ -254,3 +260,47 @@ def test_decode_step_replays_from_a_graph(lib):
                      (eager.model.k[DL - 1], graph.model.k[DL - 1])):
             assert torch.equal(a, b), t
     assert int(eager.tok.ge(0).sum()) > DB * DP   # tokens were committed
+
+
+def test_decode_loop_with_periodic_refresh_matches_the_oracle(lib):
+    """The decoding loop with a full refresh after every 3rd step (`run_step`): 8 steps against the
+    oracle doing the same; then a decoder replaying captured steps through `run_step(graph=...)`
+    against an eager one with the same schedule, bit-identical after every step."""
+    print("decode loop: refresh every 3 steps, 8 steps; graph replay with refresh", flush=True)
+    dec, w, emb, mask, prompt = decode_setup(lib, 920, refresh_every=3)
+    ref = OracleDecoder(w, emb, mask, prompt)
+    nblk = -(-(DS - DP) // DBLK)
+    for t in range(8):
+        for seed in range(4000 + 31 * t, 4000 + 31 * t + 30):
+            logits = make_logits(DB, DS, DV, seed, torch.bfloat16, spike_frac=0.15)
+            rows = Rows(logits)
+            if margins_ok(rows, ref.tok, ref.blk, DP, DBLK, DS, DKMIN, nblk):
+                break
+        dec.run_step(logits)
+        torch.cuda.synchronize()
+        sel, rp = ref.step(rows)
+        if (t + 1) % 3 == 0:
+            ref.refresh()
+        s = dec.model.step1
+        assert np.array_equal(s.row_ptr.cpu().numpy(), rp), t
+        assert np.array_equal(s.sel_idx.cpu().numpy()[:rp[-1]], sel), t
+        assert np.array_equal(dec.tok.cpu().numpy(), ref.tok), t
+        assert np.array_equal(dec.flags.cpu().numpy(), ref.flags), t
+        assert np.array_equal(host(dec.x), ref.x), t
+        assert_close(host(dec.model.hidden[DL]), ref.h[DL], 2e-2, f"step {t} output")
+        assert_close(host(dec.model.k[DL - 1]), ref.k[DL - 1], 2e-2, f"step {t} last K cache")
+    assert dec.steps_done == 8
+    eager = decode_setup(lib, 930, refresh_every=3)[0]
+    graph = decode_setup(lib, 930, refresh_every=3)[0]
+    bufs = [make_logits(DB, DS, DV, 5000 + i, torch.bfloat16, spike_frac=0.15) for i in range(3)]
+    torch.cuda.synchronize()
+    graphs = [graph.capture(b) for b in bufs]
+    torch.cuda.synchronize()
+    for t in range(7):
+        eager.run_step(bufs[t % 3])
+        graph.run_step(graph=graphs[t % 3])
+        torch.cuda.synchronize()
+        for a, b in ((eager.tok, graph.tok), (eager.flags, graph.flags), (eager.x, graph.x),
+                     (eager.model.hidden[DL], graph.model.hidden[DL]),
+                     (eager.model.k[DL - 1], graph.model.k[DL - 1])):
+            assert torch.equal(a, b), t

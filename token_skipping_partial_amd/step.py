@@ -523,14 +523,17 @@ class BlockDecoder:
     Token ids, block indices, the selection flags and the input rows live on the device and are
     updated by the library calls, so `step` never waits for the device and can be captured in a
     HIP graph (`capture`) and replayed. `refresh` is the periodic full refresh: every layer on
-    every token (the caches and the skip-layer reference rebuilt from the current input).
+    every token (the caches and the skip-layer reference rebuilt from the current input)
+    (ES-dLLM, Dutch summary page, "Methodologie" item 3: caches refreshed periodically). `run_step` is
+    one step, eager or replayed from a graph, followed by the refresh every `refresh_every` steps
+    (0 = only when called).
 
     model: EarlySkipModel whose m_cap covers B x (top-k + one block); emb [V, d] and mask_emb
     [d] in the model's dtype; the model's shape carries V (the logits' vocabulary).
     """
 
     def __init__(self, model, emb, mask_emb, prompt_len: int, block_len: int, tau: float,
-                 k_min: int, device="cuda"):
+                 k_min: int, device="cuda", refresh_every: int = 0):
         sh = model.shape
         if emb.shape != (sh.V, sh.d):
             raise ValueError(f"embedding table {tuple(emb.shape)} is not [V={sh.V}, d={sh.d}]")
@@ -539,6 +542,9 @@ class BlockDecoder:
                              "forced block")
         self.model, self.emb, self.mask_emb = model, emb, mask_emb
         self.P, self.L, self.tau, self.k_min = int(prompt_len), int(block_len), tau, int(k_min)
+        if refresh_every < 0:
+            raise ValueError(f"refresh_every {refresh_every} < 0")
+        self.refresh_every, self.steps_done = int(refresh_every), 0
         B, S = sh.B, sh.S
         self.nblk = -(-(S - self.P) // self.L)
         self.tok = torch.full((B, S), -1, dtype=torch.int32, device=device)
@@ -553,6 +559,7 @@ class BlockDecoder:
     def start(self, prompt, stream=None):
         """prompt: int32 [B, P] token ids. Every later position is masked; block 0 is active."""
         sh = self.model.shape
+        self.steps_done = 0
         self.tok.fill_(-1)
         self.tok[:, :self.P] = prompt
         self.blk.zero_()
@@ -575,6 +582,17 @@ class BlockDecoder:
     def refresh(self, stream=None):
         self.model.fill(self.x, stream)
 
+    def run_step(self, logits=None, graph=None, stream=None):
+        """One step: eager on `logits`, or the replay of `graph` (from `capture`); then the full
+        refresh if this is a multiple of `refresh_every` steps since `start`."""
+        if graph is None:
+            self.step(logits, stream)
+        else:
+            graph.replay()
+        self.steps_done += 1
+        if self.refresh_every and self.steps_done % self.refresh_every == 0:
+            self.refresh(stream)
+
     def capture(self, logits):
         """A HIP graph of one `step` reading `logits` (replay with .replay())."""
         g = torch.cuda.CUDAGraph()
@@ -588,7 +606,7 @@ class BlockDecoder:
 
     def _config(self) -> dict:
         return {"driver": "BlockDecoder", "prompt_len": self.P, "block_len": self.L,
-                "tau": float(self.tau), "k_min": self.k_min}
+                "tau": float(self.tau), "k_min": self.k_min, "refresh_every": self.refresh_every}
 
     def _carried(self) -> dict:
         return {"tok": self.tok, "blk": self.blk, "flags": self.flags, "x": self.x}
@@ -596,10 +614,11 @@ class BlockDecoder:
     def state_dict(self) -> dict:
         """Token ids, block indices, selection flags and the next step's input rows, with the
         model's state under "model"."""
-        st = _snapshot(self._config(), self._carried(), {})
+        st = _snapshot(self._config(), self._carried(), {"steps_done": self.steps_done})
         st["model"] = self.model.state_dict()
         return st
 
     def load_state_dict(self, state: dict) -> None:
-        _restore(state, self._config(), self._carried())
+        sc = _restore(state, self._config(), self._carried())
         self.model.load_state_dict(state["model"])
+        self.steps_done = int(sc["steps_done"])
